@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Bench of the online KV-cache compression hot path on one MI355X.
+
+One step = one pass of the whole path over one layer's worth of synthetic
+input: quantize the K and V vectors of every kv head into the packed caches,
+then one decode-attention step (one query per query head) over a packed cache.
+Default workload: Llama-3.1-8B-shaped layer, batch 1, 32K context, 8 kv heads,
+32 query heads, d = 128, bf16 K/V, b = 4 (3 index bits + 1 sign bit).
+
+Inputs and caches rotate through enough copies (>= 1 GiB) that neither the
+step's input nor the cache the decode reads is still in the 256 MB
+last-level cache: the decode reads a cache written several steps earlier.
+
+Prints one JSON line.  value = packed-KV decode-attention GB/s (algorithmic
+packed bytes read per decode / decode time); the quantize rate (token
+positions per second, each position = K and V of every kv head) is reported
+beside it.  Kernel durations come from HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, spec
+FP64_VEC_PEAK_TFLOPS = 78.6    # MI355X vector fp64, spec
+METRIC = "packed-KV decode-attention GB/s (% HBM peak); KV quantize tokens/s"
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_online_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("kernels", {}).get(kernel_key)
+
+
+def cpu_baseline(w, rot, proj, seconds):
+    """Time the oracle (float64 NumPy) on a bounded sample of the same workload."""
+    import oracle as O
+    import workloads as W
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max([i.get("num_threads", 0) for i in blas] + [1])
+    except Exception:
+        pass
+    cb = O.build_codebook(w.bits_mse, 1 / math.sqrt(w.d))
+    # decode: one kv head over the full context (oracle-packed cache), G query heads
+    T = w.seq_len
+    K = W.to_f64(W.kv_chunk(w, 0, 0, 0, n_tokens=T), w.dtype)
+    V = W.to_f64(W.kv_chunk(w, 1, 0, 0, n_tokens=T), w.dtype)
+    qk = O.quantize(K, rot, proj, cb)
+    qv = O.quantize(V, rot, proj, cb)
+    kp = O.pack_token_major(qk["idx"], qk["sgn"], qk["nu_bits"], qk["rho_bits"], w.bits_mse)
+    vp = O.pack_block32(qv["idx"], qv["sgn"], qv["nu_bits"], qv["rho_bits"], w.bits_mse)
+    q = W.to_f64(W.queries(w)[0, :w.group], w.dtype)
+    f16 = lambda b: np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
+    reps, t_dec = 0, 0.0
+    t_start = time.perf_counter()
+    while reps < 1 or (time.perf_counter() - t_start < seconds / 2 and reps < 20):
+        t0 = time.perf_counter()
+        i, s, nb, rb = O.unpack_token_major(*kp, w.bits_mse)
+        kh = O.dequantize(i, s, f16(nb), f16(rb), rot, proj, cb)
+        i, s, nb, rb = O.unpack_block32(*vp, w.bits_mse)
+        vh = O.dequantize(i, s, f16(nb), f16(rb), rot, proj, cb)
+        O.attention(q, kh[None], vh[None])
+        t_dec += time.perf_counter() - t0
+        reps += 1
+    rec = O.record_bytes(w.d, w.m, w.bits_mse, w.sketch)
+    dec_gbs = reps * T * 2 * rec / t_dec / 1e9
+    # quantize: token positions (K and V of every kv head) on a sample of vectors
+    n_pos = 8192
+    X = W.to_f64(W.kv_chunk(w, 0, 0, 1, n_tokens=n_pos * w.n_kv_heads * 2), w.dtype)
+    t0 = time.perf_counter()
+    qq = O.quantize(X, rot, proj, cb)
+    O.pack_token_major(qq["idx"], qq["sgn"], qq["nu_bits"], qq["rho_bits"], w.bits_mse)
+    tq = time.perf_counter() - t0
+    return {"value": dec_gbs, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": (f"decode: unpack + float64 dequantize + attention over one kv head x {T} tokens "
+                       f"(K and V), {w.group} query heads, {reps} reps, {t_dec:.1f} s; quantize: "
+                       f"{n_pos} token positions ({n_pos * w.n_kv_heads * 2} vectors), {tq:.1f} s"),
+            "quantize_tokens_per_s": n_pos / tq}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 5])
+    ap.add_argument("--copies", type=int, default=0, help="rotation copies (0: enough for 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this hot path runs on one GPU; multi-GPU runs are not part of this build "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    from kv_cache_online_amd.session import TQSession
+    from oracle import record_bytes  # layout arithmetic only, for the byte count
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = W.WORKLOADS[args.workload]
+    rot, proj = W.rotation(w.d, w.wid), W.sketch(w.m, w.d, w.wid)
+    s = TQSession(w.d, w.n_kv_heads, w.n_q_heads, rot, proj, k_bits=w.bits_mse, v_bits=w.bits_mse,
+                  k_sketch=w.sketch, v_sketch=w.sketch)
+    B, H, T, d = w.batch, w.n_kv_heads, w.seq_len, w.d
+    lens = W.seq_lengths(w)
+    cap = W.capacity(lens)
+    starts = W.seq_starts(lens)
+    esize = 4 if w.dtype == "f32" else 2
+    rec = record_bytes(d, w.m, w.bits_mse, w.sketch)
+    in_bytes = 2 * B * H * T * d * esize
+    packed_bytes = 2 * B * H * T * rec
+    footprint = in_bytes + 2 * H * cap * rec
+    R = args.copies or max(3, math.ceil((1 << 30) / footprint))
+
+    def dev(a):
+        t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        return t.view(torch.bfloat16) if a.dtype == np.uint16 else t
+
+    K0, V0 = dev(W.kv_batch(w, 0)), dev(W.kv_batch(w, 1))
+    Ks, Vs = [K0] + [K0.clone() for _ in range(R - 1)], [V0] + [V0.clone() for _ in range(R - 1)]
+    caches = [s.new_caches(cap) for _ in range(R)]
+    Q = dev(W.queries(w))
+    dst = torch.from_numpy(starts).cuda()
+    st_d = torch.from_numpy(starts).cuda()
+    ln_d = torch.from_numpy(lens.astype(np.int32)).cuda()
+    max_len = int(lens.max())
+    ws = s.workspace(B, max_len)
+    out = torch.empty(B, w.n_q_heads, d, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, evs=None):
+        r = i % R
+        kc, vc = caches[r]
+        if evs is not None:
+            evs[0].record(stream)
+        s.quantize(Ks[r], Vs[r], dst, kc, vc, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        kd, vd = caches[(r + R // 2) % R]
+        s.decode(Q, st_d, ln_d, max_len, kd, vd, out=out, workspace=ws, stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(R):          # populate every cache copy
+        step(i)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    qt = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
+    dt_ = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
+    assert torch.isfinite(out).all(), "decode produced non-finite output"
+    status = int(s.status.item()) & 0xFFFFFFFF
+    assert status == 0, f"device status flags {status:#x}"
+
+    q_avg, d_avg = float(qt.mean()), float(dt_.mean())
+    dec_gbs = packed_bytes / d_avg / 1e9
+    q_bytes = in_bytes + packed_bytes
+    q_gbs = q_bytes / q_avg / 1e9
+    q_tok = B * T / q_avg
+    q_flops = 2 * B * H * T * 4 * d * d           # two d x d contractions per vector
+    roof_dec = {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dec_gbs / HBM_PEAK_GBS, "traffic": traffic_for("decode"),
+                "kernel": "tq_decode_attention (query prep + split partials + merge)",
+                "bytes_per_launch": packed_bytes, "avg_launch_s": d_avg}
+    roof_q_hbm = {"bound": "hbm", "achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": q_gbs / HBM_PEAK_GBS}
+    q_tf = q_flops / q_avg / 1e12
+    roof_q = {"bound": "alu", "achieved": q_tf, "peak": FP64_VEC_PEAK_TFLOPS, "unit": "TFLOP/s",
+              "frac": q_tf / FP64_VEC_PEAK_TFLOPS, "traffic": traffic_for("quantize"),
+              "kernel": "tq_quantize_kv (K and V launches)", "flops_per_launch": q_flops,
+              "bytes_per_launch": q_bytes, "avg_launch_s": q_avg, "hbm": roof_q_hbm}
+    dominant = roof_q if q_avg >= d_avg else roof_dec
+    res = {
+        "metric": METRIC, "value": dec_gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": (t1 - t0) / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded Gaussian K/V/Q with per-channel scales and outlier channels)",
+        "config": {"workload": w.name, "batch": B, "kv_heads": H, "q_heads": w.n_q_heads, "seq_len": T,
+                   "head_dim": d, "bits": w.bits, "input_dtype": w.dtype, "rotation_copies": R},
+        "decode_pct_hbm_peak": 100 * dec_gbs / HBM_PEAK_GBS,
+        "quantize_tokens_per_s": q_tok, "quantize_GBps": q_gbs,
+        "roofline": dominant, "roofline_decode": roof_dec, "roofline_quantize": roof_q,
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, rot, proj, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

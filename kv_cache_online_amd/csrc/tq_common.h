@@ -1,0 +1,118 @@
+// Internal declarations shared by the libtq translation units (not part of the ABI).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "tq.h"
+
+namespace tq {
+
+// ---------------------------------------------------------------- prep blob --
+// Device-side matrices derived on the host from Pi and S (d == m):
+//   rotT   fp32 [d][d]   rotT[k][j] = Pi[j][k]
+//   stT    fp32 [d][m]   stT[j][i]  = S~[i][j],  S~ = S Pi^T (float64, then fp32)
+//   projT  fp32 [d][m]   projT[k][i] = S[i][k]
+//   rot_hml bf16 [3][d][d]  Pi split hi/mid/lo (hi + mid + lo == fp32 Pi exactly)
+//   st_hml  bf16 [3][m][d]  S~ split hi/mid/lo
+//   stnorm fp32 [m]      row norms ||S~_i||_2
+// Every section starts on a 256-byte boundary after a 256-byte header.
+struct PrepLayout {
+  size_t rotT, stT, projT, rot_hml, st_hml, stnorm, total;
+};
+
+constexpr uint32_t kPrepMagic = 0x31505154u;  // "TQP1"
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline PrepLayout prep_layout(int d, int m) {
+  PrepLayout L{};
+  size_t o = 256;
+  L.rotT = o;    o = align256(o + size_t(d) * d * 4);
+  L.stT = o;     o = align256(o + size_t(d) * m * 4);
+  L.projT = o;   o = align256(o + size_t(d) * m * 4);
+  L.rot_hml = o; o = align256(o + size_t(3) * d * d * 2);
+  L.st_hml = o;  o = align256(o + size_t(3) * m * d * 2);
+  L.stnorm = o;  o = align256(o + size_t(m) * 4);
+  L.total = o;
+  return L;
+}
+
+// --------------------------------------------------------------- decode plan --
+// Token splits of the decode partial pass.  The same plan sizes the workspace
+// and the launch, so both derive it from (batch, kv heads, max_len) alone.
+struct DecodePlan {
+  int32_t split_tokens;  // tokens per split, a multiple of 64
+  int32_t n_split;       // splits per (sequence, kv head)
+  size_t off_qr, off_qs, off_part, total;  // workspace byte offsets
+  int32_t part_stride;   // floats per partial record: 2 + d + m
+};
+
+DecodePlan decode_plan(const tq_config &cfg, int32_t batch, int32_t max_len);
+
+// ----------------------------------------------------- kernel-side arguments --
+struct CodebookF32 {
+  float thr[TQ_MAX_LEVELS - 1];
+  float cen[TQ_MAX_LEVELS];
+  int32_t levels;
+};
+
+struct QuantTensorArgs {
+  const void *x;         // [batch][H][n_new][d]
+  uint32_t *idx;
+  uint32_t *sgn;
+  uint16_t *scl;
+  int64_t cap;
+  int32_t layout;
+  int32_t bq;            // b'
+  int32_t sketch;
+  CodebookF32 cb;
+  float *dbg;            // [batch][H][n_new][2] or null
+};
+
+struct QuantArgs {
+  QuantTensorArgs t;
+  int32_t dtype;         // tq_dtype
+  int32_t batch, H, n_new;
+  const int64_t *dst;
+  const float *rotT;
+  const float *stT;
+  uint32_t *status;
+};
+
+struct DecodeTensorArgs {
+  const uint32_t *idx;
+  const uint32_t *sgn;
+  const uint16_t *scl;
+  int64_t cap;
+  int32_t bq;
+  int32_t sketch;
+  CodebookF32 cb;
+};
+
+struct DecodeArgs {
+  DecodeTensorArgs k, v;
+  const void *q;         // [batch][Hq][d]
+  int32_t dtype;
+  int32_t batch, Hkv, Hq, G;
+  const int64_t *seq_start;
+  const int32_t *seq_len;
+  float sm_scale;
+  float kappa;           // sqrt(pi/2) / m
+  const float *rot;      // Pi [d][d]
+  const float *proj;     // S [m][d]
+  const float *rotT;
+  const float *projT;
+  float *qr;             // [batch][Hq][d]
+  float *qs;             // [batch][Hq][m]
+  float *part;           // [batch][Hq][n_split][2 + d + m]
+  int32_t split_tokens, n_split;
+  float *out;            // [batch][Hq][d]
+  uint32_t *status;
+};
+
+// Host launchers (defined in the .hip translation units).  Return hipError_t.
+int launch_quantize(int d, const QuantArgs &a, hipStream_t s);
+int launch_decode(int d, const DecodeArgs &a, hipStream_t s);
+
+}  // namespace tq

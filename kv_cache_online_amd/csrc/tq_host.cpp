@@ -1,0 +1,373 @@
+// Host side of libtq: Lloyd-Max codebook, matrix precomputation, argument
+// validation and the extern "C" entry points declared in tq.h.
+//
+// Sources: ast-softpro.ru, "Технология TurboQuant и её применение с локальными
+// LLM", section 1.2 "Как работает TurboQuant" (stage 1: random orthogonal
+// rotation and a b-1 bit MSE-optimal Lloyd-Max quantizer per coordinate;
+// stage 2: sign of a Gaussian projection of the residual, plus ||r||_2);
+// kiosknews.app, "3 бита вместо 16: разбираем TurboQuant и когда его реально
+// стоит включать", section "Как работает TurboQuant" (the codebook is computed
+// once for the known post-rotation distribution and stored).
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "tq_common.h"
+
+namespace {
+
+// --------------------------------------------------------------- Lloyd-Max --
+// Standard normal density and the probability of a cell [a, b), taken on the
+// side of the smaller tail so that cells far out keep full relative precision.
+double npdf(double x) {
+  if (std::isinf(x)) return 0.0;
+  return std::exp(-0.5 * x * x) * 0.39894228040143267794;  // 1/sqrt(2 pi)
+}
+double upper_tail(double x) {  // P(X >= x)
+  if (x == INFINITY) return 0.0;
+  if (x == -INFINITY) return 1.0;
+  return 0.5 * std::erfc(x * 0.70710678118654752440);
+}
+double cell_prob(double a, double b) {
+  if (a > 0) return upper_tail(a) - upper_tail(b);
+  return upper_tail(-b) - upper_tail(-a);  // P(-b < X <= -a) by symmetry
+}
+
+uint16_t bf16_rne(double v) {
+  float f = static_cast<float>(v);  // v is exactly representable or a remainder
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  uint32_t lsb = (u >> 16) & 1u;
+  return static_cast<uint16_t>((u + 0x7FFFu + lsb) >> 16);
+}
+double bf16_val(uint16_t b) {
+  uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+void split3(float v, uint16_t *hi, uint16_t *mid, uint16_t *lo) {
+  double r = v;
+  *hi = bf16_rne(r);
+  r -= bf16_val(*hi);
+  *mid = bf16_rne(r);
+  r -= bf16_val(*mid);
+  *lo = bf16_rne(r);
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
+
+int check_spec(const tq_tensor_spec &s, int d) {
+  if (s.bits_mse < 1 || s.bits_mse > 3) return TQ_ERR_INVALID_ARG;
+  if (s.sketch != 0 && s.sketch != 1) return TQ_ERR_INVALID_ARG;
+  if (s.cb.bits_mse != s.bits_mse || s.cb.levels != (1 << s.bits_mse)) return TQ_ERR_INVALID_ARG;
+  (void)d;
+  return TQ_OK;
+}
+
+int check_config(const tq_config *cfg) {
+  if (!cfg) return TQ_ERR_INVALID_ARG;
+  if (cfg->d <= 0 || cfg->m != cfg->d) return TQ_ERR_INVALID_ARG;
+  if (!supported_d(cfg->d)) return TQ_ERR_UNSUPPORTED;
+  if (cfg->n_kv_heads <= 0 || cfg->n_q_heads <= 0 || cfg->n_q_heads % cfg->n_kv_heads)
+    return TQ_ERR_INVALID_ARG;
+  if (!cfg->rot || !cfg->proj || !cfg->prep) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(cfg->rot) || !aligned16(cfg->proj) || !aligned16(cfg->prep)) return TQ_ERR_INVALID_ARG;
+  int e = check_spec(cfg->k, cfg->d);
+  if (e) return e;
+  return check_spec(cfg->v, cfg->d);
+}
+
+int check_cache(const tq_cache *c, const tq_tensor_spec &s) {
+  if (!c || !c->idx || !c->scl) return TQ_ERR_INVALID_ARG;
+  if (s.sketch && !c->sgn) return TQ_ERR_INVALID_ARG;
+  if (c->capacity <= 0 || c->capacity % 32) return TQ_ERR_INVALID_ARG;
+  if (c->layout != TQ_LAYOUT_TOKEN_MAJOR && c->layout != TQ_LAYOUT_BLOCK32) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(c->idx) || !aligned16(c->scl) || (c->sgn && !aligned16(c->sgn))) return TQ_ERR_INVALID_ARG;
+  return TQ_OK;
+}
+
+tq::CodebookF32 cb_f32(const tq_codebook &cb) {
+  tq::CodebookF32 o{};
+  for (int i = 0; i < TQ_MAX_LEVELS - 1; ++i) o.thr[i] = cb.boundary_f32[i];
+  for (int i = 0; i < TQ_MAX_LEVELS; ++i) o.cen[i] = cb.centroid_f32[i];
+  o.levels = cb.levels;
+  return o;
+}
+
+}  // namespace
+
+namespace tq {
+
+DecodePlan decode_plan(const tq_config &cfg, int32_t batch, int32_t max_len) {
+  DecodePlan p{};
+  const int64_t pairs = int64_t(batch) * cfg.n_kv_heads;
+  const int64_t want_wg = 2048;
+  int64_t ns = pairs > 0 ? (want_wg + pairs - 1) / pairs : 1;
+  if (ns < 1) ns = 1;
+  int64_t st = max_len > 0 ? (int64_t(max_len) + ns - 1) / ns : 64;
+  if (st < 256) st = 256;
+  st = (st + 63) / 64 * 64;
+  p.split_tokens = static_cast<int32_t>(st);
+  p.n_split = max_len > 0 ? static_cast<int32_t>((int64_t(max_len) + st - 1) / st) : 1;
+  p.part_stride = 2 + cfg.d + cfg.m;
+  const size_t nq = size_t(batch) * cfg.n_q_heads;
+  size_t o = 0;
+  p.off_qr = o;   o = align256(o + nq * cfg.d * 4);
+  p.off_qs = o;   o = align256(o + nq * cfg.m * 4);
+  p.off_part = o; o = align256(o + nq * size_t(p.n_split) * p.part_stride * 4);
+  p.total = o;
+  return p;
+}
+
+}  // namespace tq
+
+extern "C" {
+
+const char *tq_status_string(int s) {
+  switch (s) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TQ_ERR_WORKSPACE: return "workspace too small";
+    case TQ_ERR_LAUNCH: return "kernel launch failed";
+    case TQ_ERR_NO_CONVERGENCE: return "Lloyd-Max did not converge";
+    default: return "unknown status";
+  }
+}
+
+int tq_build_codebook(int32_t bits_mse, double sigma, tq_codebook *out) {
+  if (!out || bits_mse < 1 || bits_mse > 3 || !(sigma > 0) || !std::isfinite(sigma))
+    return TQ_ERR_INVALID_ARG;
+  const int L = 1 << bits_mse;
+  double c[TQ_MAX_LEVELS], t[TQ_MAX_LEVELS + 1];
+  // start from an evenly spaced symmetric grid (N(0,1) units)
+  for (int k = 0; k < L; ++k) c[k] = (2.0 * k - (L - 1)) / L * 2.0;
+  int it = 0;
+  bool done = false;
+  for (it = 1; it <= 100000; ++it) {
+    t[0] = -INFINITY;
+    t[L] = INFINITY;
+    for (int k = 1; k < L; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);  // midpoint condition
+    double delta = 0.0;
+    for (int k = 0; k < L; ++k) {  // centroid condition: conditional mean of the cell
+      double nc = (npdf(t[k]) - npdf(t[k + 1])) / cell_prob(t[k], t[k + 1]);
+      delta = std::fmax(delta, std::fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (delta <= 1e-15) { done = true; break; }
+  }
+  if (!done) return TQ_ERR_NO_CONVERGENCE;
+  double cs[TQ_MAX_LEVELS];
+  for (int k = 0; k < L; ++k) cs[k] = 0.5 * (c[k] - c[L - 1 - k]);  // exact antisymmetry
+  std::memset(out, 0, sizeof(*out));
+  out->bits_mse = bits_mse;
+  out->levels = L;
+  out->sigma = sigma;
+  double mse = 1.0;
+  t[0] = -INFINITY;
+  t[L] = INFINITY;
+  for (int k = 1; k < L; ++k) t[k] = 0.5 * (cs[k - 1] + cs[k]);
+  for (int k = 0; k < L; ++k) mse -= cell_prob(t[k], t[k + 1]) * cs[k] * cs[k];
+  for (int k = 0; k < L; ++k) {
+    out->centroid[k] = cs[k] * sigma;
+    out->centroid_f32[k] = static_cast<float>(out->centroid[k]);
+  }
+  for (int k = 0; k + 1 < L; ++k) {
+    out->boundary[k] = t[k + 1] * sigma;
+    out->boundary_f32[k] = static_cast<float>(out->boundary[k]);
+  }
+  // Walsh expansion over index bit-planes: walsh[S] = mean_i c[i] prod_{p in S} s_p(i).
+  // Code L-1-i has every bit of i flipped and c[L-1-i] = -c[i], so the pair
+  // (i, L-1-i) cancels for even |S| and doubles for odd |S|.
+  for (int S = 0; S < L; ++S) {
+    if (!(__builtin_popcount(S) & 1)) {
+      out->walsh[S] = 0.0;
+      continue;
+    }
+    double acc = 0.0;
+    for (int i = 0; i < L / 2; ++i) {
+      double sgn = 1.0;
+      for (int p = 0; p < bits_mse; ++p)
+        if (S >> p & 1) sgn *= (i >> p & 1) ? 1.0 : -1.0;
+      acc += out->centroid[i] * sgn;
+    }
+    out->walsh[S] = 2.0 * acc / L;
+  }
+  out->mse = mse * sigma * sigma;
+  out->iterations = it;
+  return TQ_OK;
+}
+
+size_t tq_prepare_bytes(int32_t d, int32_t m) {
+  if (m != d || !supported_d(d)) return 0;
+  return tq::prep_layout(d, m).total;
+}
+
+int tq_prepare(const float *rot, const float *proj, int32_t d, int32_t m, void *blob) {
+  if (!rot || !proj || !blob || d <= 0 || m != d) return TQ_ERR_INVALID_ARG;
+  if (!supported_d(d)) return TQ_ERR_UNSUPPORTED;
+  const tq::PrepLayout L = tq::prep_layout(d, m);
+  auto *base = static_cast<unsigned char *>(blob);
+  std::memset(base, 0, L.total);
+  uint32_t hdr[4] = {tq::kPrepMagic, 1u, static_cast<uint32_t>(d), static_cast<uint32_t>(m)};
+  std::memcpy(base, hdr, sizeof(hdr));
+  auto *rotT = reinterpret_cast<float *>(base + L.rotT);
+  auto *stT = reinterpret_cast<float *>(base + L.stT);
+  auto *projT = reinterpret_cast<float *>(base + L.projT);
+  auto *rot_hml = reinterpret_cast<uint16_t *>(base + L.rot_hml);
+  auto *st_hml = reinterpret_cast<uint16_t *>(base + L.st_hml);
+  auto *stnorm = reinterpret_cast<float *>(base + L.stnorm);
+  const size_t dd = size_t(d) * d, md = size_t(m) * d;
+  for (int j = 0; j < d; ++j)
+    for (int k = 0; k < d; ++k) {
+      rotT[size_t(k) * d + j] = rot[size_t(j) * d + k];
+      split3(rot[size_t(j) * d + k], &rot_hml[size_t(j) * d + k], &rot_hml[dd + size_t(j) * d + k],
+             &rot_hml[2 * dd + size_t(j) * d + k]);
+    }
+  for (int i = 0; i < m; ++i)
+    for (int k = 0; k < d; ++k) projT[size_t(k) * m + i] = proj[size_t(i) * d + k];
+  // S~ = S Pi^T in float64: S~[i][j] = sum_k S[i][k] Pi[j][k]
+  std::vector<double> st(md);
+  for (int i = 0; i < m; ++i)
+    for (int j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (int k = 0; k < d; ++k) acc += double(proj[size_t(i) * d + k]) * double(rot[size_t(j) * d + k]);
+      st[size_t(i) * d + j] = acc;
+    }
+  for (int i = 0; i < m; ++i) {
+    double nrm = 0.0;
+    for (int j = 0; j < d; ++j) {
+      float f = static_cast<float>(st[size_t(i) * d + j]);
+      stT[size_t(j) * m + i] = f;
+      split3(f, &st_hml[size_t(i) * d + j], &st_hml[md + size_t(i) * d + j], &st_hml[2 * md + size_t(i) * d + j]);
+      nrm += double(f) * double(f);
+    }
+    stnorm[i] = static_cast<float>(std::sqrt(nrm));
+  }
+  return TQ_OK;
+}
+
+int tq_quantize_kv(const tq_config *cfg, const void *k, const void *v, tq_dtype dt, int32_t batch,
+                   int32_t n_new, const int64_t *dst_token, const tq_cache *kc, const tq_cache *vc,
+                   uint32_t *status, float *dbg_scales, hipStream_t stream) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (dt != TQ_F32 && dt != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (batch < 0 || n_new < 0) return TQ_ERR_INVALID_ARG;
+  if (!k && !v) return TQ_ERR_INVALID_ARG;
+  if (int64_t(batch) * n_new == 0) return TQ_OK;
+  if (!dst_token) return TQ_ERR_INVALID_ARG;
+  if ((status && (reinterpret_cast<uintptr_t>(status) & 3u)) || (dbg_scales && !aligned16(dbg_scales)))
+    return TQ_ERR_INVALID_ARG;
+  if ((k && !aligned16(k)) || (v && !aligned16(v)) || (reinterpret_cast<uintptr_t>(dst_token) & 7u))
+    return TQ_ERR_INVALID_ARG;
+  if (k && (e = check_cache(kc, cfg->k))) return e;
+  if (v && (e = check_cache(vc, cfg->v))) return e;
+  const tq::PrepLayout L = tq::prep_layout(cfg->d, cfg->m);
+  const auto *prep = static_cast<const unsigned char *>(cfg->prep);
+  const size_t per_tensor = size_t(batch) * cfg->n_kv_heads * n_new * 2;
+  for (int t = 0; t < 2; ++t) {
+    const void *x = t ? v : k;
+    if (!x) continue;
+    const tq_cache *c = t ? vc : kc;
+    const tq_tensor_spec &s = t ? cfg->v : cfg->k;
+    tq::QuantArgs a{};
+    a.t.x = x;
+    a.t.idx = c->idx;
+    a.t.sgn = c->sgn;
+    a.t.scl = c->scl;
+    a.t.cap = c->capacity;
+    a.t.layout = c->layout;
+    a.t.bq = s.bits_mse;
+    a.t.sketch = s.sketch;
+    a.t.cb = cb_f32(s.cb);
+    a.t.dbg = dbg_scales ? dbg_scales + t * per_tensor : nullptr;
+    a.dtype = dt;
+    a.batch = batch;
+    a.H = cfg->n_kv_heads;
+    a.n_new = n_new;
+    a.dst = dst_token;
+    a.rotT = reinterpret_cast<const float *>(prep + L.rotT);
+    a.stT = reinterpret_cast<const float *>(prep + L.stT);
+    a.status = status;
+    if (tq::launch_quantize(cfg->d, a, stream) != 0) return TQ_ERR_LAUNCH;
+  }
+  return TQ_OK;
+}
+
+size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t max_len) {
+  if (!cfg || batch < 0 || max_len < 0 || cfg->d <= 0 || cfg->m != cfg->d || cfg->n_kv_heads <= 0)
+    return 0;
+  return tq::decode_plan(*cfg, batch, max_len).total;
+}
+
+int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_t batch,
+                        const int64_t *seq_start, const int32_t *seq_len, int32_t max_len,
+                        const tq_cache *kc, const tq_cache *vc, float sm_scale, float *out,
+                        uint32_t *status, void *workspace, size_t ws_bytes, hipStream_t stream) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (dt != TQ_F32 && dt != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (batch < 0 || max_len < 0) return TQ_ERR_INVALID_ARG;
+  if (batch == 0) return TQ_OK;
+  if (!q || !seq_start || !seq_len || !out || !workspace) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return TQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(seq_start) & 7u) || (reinterpret_cast<uintptr_t>(seq_len) & 3u))
+    return TQ_ERR_INVALID_ARG;
+  if (status && (reinterpret_cast<uintptr_t>(status) & 3u)) return TQ_ERR_INVALID_ARG;
+  if ((e = check_cache(kc, cfg->k)) || (e = check_cache(vc, cfg->v))) return e;
+  if (kc->layout != TQ_LAYOUT_TOKEN_MAJOR || vc->layout != TQ_LAYOUT_BLOCK32) return TQ_ERR_UNSUPPORTED;
+  if (!(sm_scale >= 0) || !std::isfinite(sm_scale)) return TQ_ERR_INVALID_ARG;
+  const int G = cfg->n_q_heads / cfg->n_kv_heads;
+  if (G > 16 || (G & (G - 1))) return TQ_ERR_UNSUPPORTED;
+  const tq::DecodePlan p = tq::decode_plan(*cfg, batch, max_len);
+  if (ws_bytes < p.total) return TQ_ERR_WORKSPACE;
+  const tq::PrepLayout L = tq::prep_layout(cfg->d, cfg->m);
+  const auto *prep = static_cast<const unsigned char *>(cfg->prep);
+  auto *ws = static_cast<unsigned char *>(workspace);
+  tq::DecodeArgs a{};
+  for (int t = 0; t < 2; ++t) {
+    const tq_cache *c = t ? vc : kc;
+    const tq_tensor_spec &s = t ? cfg->v : cfg->k;
+    tq::DecodeTensorArgs &ta = t ? a.v : a.k;
+    ta.idx = c->idx;
+    ta.sgn = c->sgn;
+    ta.scl = c->scl;
+    ta.cap = c->capacity;
+    ta.bq = s.bits_mse;
+    ta.sketch = s.sketch;
+    ta.cb = cb_f32(s.cb);
+  }
+  a.q = q;
+  a.dtype = dt;
+  a.batch = batch;
+  a.Hkv = cfg->n_kv_heads;
+  a.Hq = cfg->n_q_heads;
+  a.G = G;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.sm_scale = sm_scale > 0 ? sm_scale : static_cast<float>(1.0 / std::sqrt(double(cfg->d)));
+  a.kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / cfg->m);
+  a.rot = cfg->rot;
+  a.proj = cfg->proj;
+  a.rotT = reinterpret_cast<const float *>(prep + L.rotT);
+  a.projT = reinterpret_cast<const float *>(prep + L.projT);
+  a.qr = reinterpret_cast<float *>(ws + p.off_qr);
+  a.qs = reinterpret_cast<float *>(ws + p.off_qs);
+  a.part = reinterpret_cast<float *>(ws + p.off_part);
+  a.split_tokens = p.split_tokens;
+  a.n_split = p.n_split;
+  a.out = out;
+  a.status = status;
+  if (tq::launch_decode(cfg->d, a, stream) != 0) return TQ_ERR_LAUNCH;
+  return TQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,316 @@
+"""GPU parity: libtq quantize and decode against the CPU oracle (needs an MI355X).
+
+Reduced shapes span several tiles with ragged tails and are compared entry by
+entry; the full workload shapes are compared on sampled vectors and on sampled
+(sequence, kv head) decode outputs, which the oracle recomputes from the packed
+bytes the device wrote.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+import _parity as PR  # noqa: E402
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+class Run:
+    """One workload instance on the device: inputs, caches, quantize, decode."""
+
+    def __init__(self, w, batch=None, n_tokens=None, lens=None, k_bits=None, v_bits=None,
+                 k_sketch=None, v_sketch=None, extra=0):
+        from kv_cache_online_amd.session import TQSession
+        _need_gpu()
+        self.w = w
+        self.batch = w.batch if batch is None else batch
+        T = w.seq_len if n_tokens is None else n_tokens
+        self.lens = np.full(self.batch, T, np.int64) if lens is None else np.asarray(lens, np.int64)
+        self.T = int(self.lens.max())
+        self.starts = W.seq_starts(self.lens)
+        self.cap = W.capacity(self.lens)
+        self.k_bits = w.bits_mse if k_bits is None else k_bits
+        self.v_bits = w.bits_mse if v_bits is None else v_bits
+        self.k_sketch = w.sketch if k_sketch is None else k_sketch
+        self.v_sketch = w.sketch if v_sketch is None else v_sketch
+        self.rot = W.rotation(w.d, w.wid)
+        self.proj = W.sketch(w.m, w.d, w.wid)
+        self.cb_k = O.build_codebook(self.k_bits, 1 / math.sqrt(w.d))
+        self.cb_v = O.build_codebook(self.v_bits, 1 / math.sqrt(w.d))
+        self.s = TQSession(w.d, w.n_kv_heads, w.n_q_heads, self.rot, self.proj, k_bits=self.k_bits,
+                           v_bits=self.v_bits, k_sketch=self.k_sketch, v_sketch=self.v_sketch)
+        self.kc, self.vc = self.s.new_caches(self.cap)
+        self.K = W.kv_batch(w, 0, n_tokens=self.T + extra, batch=self.batch)
+        self.V = W.kv_batch(w, 1, n_tokens=self.T + extra, batch=self.batch)
+        self.Q = W.queries(w)[: self.batch]
+
+    def dev(self, a):
+        t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        return t.view(torch.bfloat16) if a.dtype == np.uint16 else t
+
+    def quantize(self, K=None, V=None, dst=None, n_new=None):
+        K = self.K if K is None else K
+        V = self.V if V is None else V
+        dst = self.starts if dst is None else dst
+        kd, vd = self.dev(K), self.dev(V)
+        b, h, n, d = K.shape
+        self.dbg = torch.zeros(2 * b * h * n * 2, dtype=torch.float32, device="cuda")
+        self.s.quantize(kd, vd, torch.from_numpy(np.asarray(dst, np.int64)).cuda(), self.kc, self.vc, dbg=self.dbg)
+        torch.cuda.synchronize()
+        return self.dbg.cpu().numpy().reshape(2, b, h, n, 2)
+
+    def host_caches(self):
+        return self.kc.host_arrays(), self.vc.host_arrays()
+
+    def decode(self, lens=None, starts=None, max_len=None):
+        lens = self.lens if lens is None else np.asarray(lens, np.int64)
+        starts = self.starts if starts is None else starts
+        q = self.dev(self.Q)
+        ml = int(lens.max()) if max_len is None else max_len
+        out = self.s.decode(q, torch.from_numpy(np.asarray(starts, np.int64)).cuda(),
+                            torch.from_numpy(lens.astype(np.int32)).cuda(), ml, self.kc, self.vc)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64)
+
+    def status(self):
+        return int(self.s.status.cpu().numpy()[0]) & 0xFFFFFFFF
+
+
+def check_quantize(run, dbg, samples=None, T=None, K=None, V=None, starts=None, label=""):
+    """Compare (tensor, seq, head, token) vectors; samples=None means every vector."""
+    w = run.w
+    K = run.K if K is None else K
+    V = run.V if V is None else V
+    starts = run.starts if starts is None else starts
+    caches = run.host_caches()
+    reps = []
+    for tensor, X, bits, sk, cb, layout in ((0, K, run.k_bits, run.k_sketch, run.cb_k, 0),
+                                            (1, V, run.v_bits, run.v_sketch, run.cb_v, 1)):
+        idx_w, sgn_w, scl = caches[tensor]
+        b, h, n, d = X.shape
+        if samples is None:
+            sel = [(s, hh, np.arange(n)) for s in range(b) for hh in range(h)]
+        else:
+            rng = np.random.default_rng(samples)
+            sel = []
+            for s in range(b):
+                for hh in range(h):
+                    sel.append((s, hh, np.sort(rng.choice(n, size=min(n, 64), replace=False))))
+        xs, gi, gs, gnb, grb, gdbg = [], [], [], [], [], []
+        for s, hh, toks in sel:
+            slots = starts[s] + toks
+            i, sg, nb, rb = PR.unpack_tokens(idx_w, sgn_w, scl, layout, hh, slots, bits)
+            xs.append(W.to_f64(X[s, hh, toks], w.dtype))
+            gi.append(i)
+            gs.append(sg if sk else np.zeros((len(toks), d), bool))
+            gnb.append(nb)
+            grb.append(rb)
+            gdbg.append(dbg[tensor, s, hh, toks])
+        rep = PR.quantize_parity(np.concatenate(xs), run.rot, run.proj, cb, np.concatenate(gi),
+                                 np.concatenate(gs), np.concatenate(gnb), np.concatenate(grb),
+                                 np.concatenate(gdbg), sketch=bool(sk), label=f"{label} tensor {tensor}")
+        _log(PR.summary(rep))
+        assert rep["ok"], PR.summary(rep)
+        reps.append(rep)
+    return reps
+
+
+def check_decode(run, out, pairs=None, lens=None, starts=None, label=""):
+    w = run.w
+    G = w.group
+    lens = run.lens if lens is None else lens
+    starts = run.starts if starts is None else starts
+    kcache, vcache = run.host_caches()
+    if pairs is None:
+        pairs = [(s, h) for s in range(run.batch) for h in range(w.n_kv_heads)]
+    worst = 0.0
+    for s, h in pairs:
+        q64 = W.to_f64(run.Q[s, h * G:(h + 1) * G], w.dtype)
+        n = int(lens[s])
+        if n == 0:
+            np.testing.assert_array_equal(out[s, h * G:(h + 1) * G], 0.0)
+            continue
+        ref = PR.decode_reference(q64, kcache, vcache, run.k_bits, run.v_bits, run.k_sketch, run.v_sketch,
+                                  run.rot, run.proj, run.cb_k, run.cb_v, int(starts[s]), n, [h])
+        vmax = np.max(np.abs(W.to_f64(run.V[s, h, :min(n, run.V.shape[2])], w.dtype)))
+        err = np.max(np.abs(out[s, h * G:(h + 1) * G] - ref))
+        worst = max(worst, err / vmax)
+        assert err <= 1e-4 * vmax, (label, s, h, err, vmax)
+    _log({"label": label, "decode_pairs": len(pairs), "worst_err_over_maxV": worst})
+    return worst
+
+
+# ------------------------------------------------------- reduced workloads ---
+def test_workload1_full():
+    w = W.WORKLOADS[1]
+    run = Run(w)
+    _log("workload 1 full: quantize")
+    dbg = run.quantize()
+    check_quantize(run, dbg, label="w1")
+    _log("workload 1 full: decode")
+    check_decode(run, run.decode(), label="w1")
+    assert run.status() == 0
+
+
+@pytest.mark.parametrize("wid,batch,T", [(2, 1, 1000), (3, 2, 777), (5, 2, 513)])
+def test_reduced_workloads(wid, batch, T):
+    w = W.WORKLOADS[wid]
+    run = Run(w, batch=batch, n_tokens=T)
+    _log(f"workload {wid} reduced T={T}: quantize")
+    dbg = run.quantize()
+    check_quantize(run, dbg, label=f"w{wid}-T{T}")
+    _log(f"workload {wid} reduced: decode")
+    check_decode(run, run.decode(), label=f"w{wid}-T{T}")
+    assert run.status() == 0
+
+
+def test_ragged_incremental_reduced():
+    """Ragged lengths, then one appended token per sequence at its current end."""
+    w = W.WORKLOADS[4]
+    lens = np.random.default_rng(3).integers(1, 700, size=5)
+    run = Run(w, batch=5, lens=lens, extra=1)
+    K = run.K.copy()
+    V = run.V.copy()
+    for s in range(5):  # positions past each sequence's own length are not written
+        K[s, :, lens[s]:] = 0
+        V[s, :, lens[s]:] = 0
+    # prefill: quantize each sequence's own tokens only
+    for s in range(5):
+        run.quantize(K=K[s:s + 1, :, :lens[s]], V=V[s:s + 1, :, :lens[s]], dst=run.starts[s:s + 1])
+    newk = np.stack([np.stack([W.new_tokens(w, 0, s, h) for h in range(w.n_kv_heads)]) for s in range(5)])
+    newv = np.stack([np.stack([W.new_tokens(w, 1, s, h) for h in range(w.n_kv_heads)]) for s in range(5)])
+    dst = run.starts + lens
+    _log("ragged reduced: incremental quantize")
+    dbg = run.quantize(K=newk, V=newv, dst=dst)
+    check_quantize(run, dbg, K=newk, V=newv, starts=dst, label="w4-incremental")
+    # the cache now holds len + 1 tokens per sequence
+    for s in range(5):
+        L = lens[s]
+        run.K[s, :, L] = newk[s, :, 0]
+        run.V[s, :, L] = newv[s, :, 0]
+    lens1 = lens + 1
+    out = run.decode(lens=lens1)
+    check_decode(run, out, lens=lens1, label="w4-reduced")
+    assert run.status() == 0
+
+
+def test_mse_only_and_asymmetric_bits():
+    """Keys with 3+1 bits, values MSE-only with 2 bits (and the reverse)."""
+    w = W.WORKLOADS[2]
+    for kb, vb, ks, vs in ((3, 2, 1, 0), (1, 3, 0, 1)):
+        run = Run(w, batch=1, n_tokens=300, k_bits=kb, v_bits=vb, k_sketch=ks, v_sketch=vs)
+        _log(f"asymmetric k{kb}{'+s' if ks else ''} v{vb}{'+s' if vs else ''}")
+        dbg = run.quantize()
+        check_quantize(run, dbg, label=f"k{kb}s{ks}-v{vb}s{vs}")
+        check_decode(run, run.decode(), label=f"k{kb}s{ks}-v{vb}s{vs}")
+
+
+# -------------------------------------------------------------- edge cases ---
+def test_edge_cases():
+    w = W.small(W.WORKLOADS[2], n_kv_heads=1, n_q_heads=4)
+    run = Run(w, batch=3, n_tokens=64)
+    K, V = run.K.copy(), run.V.copy()
+    K[0, 0, 5] = 0                                   # zero vector
+    V[0, 0, 9] = 0
+    dbg = run.quantize(K=K, V=V)
+    run.K, run.V = K, V
+    check_quantize(run, dbg, label="edges")
+    # length 0 -> zeros; length 1 -> the first token's value; length 64 -> full
+    lens = np.array([0, 1, 64])
+    out = run.decode(lens=lens)
+    check_decode(run, out, lens=lens, label="edges-len")
+    assert np.all(out[0] == 0)
+    assert run.status() == 0
+    # NaN input and a norm above the fp16 range set status flags
+    K2 = K.copy()
+    K2[1, 0, 3, 7] = W.f32_to_bf16_bits(np.array([np.nan], np.float32))[0]
+    V2 = V.copy()
+    V2[2, 0, 4] = W.f32_to_bf16_bits(np.full(w.d, 1.0e4, np.float32))
+    run.quantize(K=K2, V=V2)
+    st = run.status()
+    assert st & 1 and st & 2
+    vscl = run.vc.host_arrays()[2]
+    assert vscl[0, run.starts[2] + 4, 0] == 0x7BFF
+    # an out-of-range slot is skipped and flagged; the cache is left as it was
+    run.s.status.zero_()
+    before = [a.copy() for a in run.kc.host_arrays() if a is not None]
+    run.quantize(K=K[:1, :, :1], V=V[:1, :, :1], dst=np.array([run.cap]))
+    assert run.status() & 4
+    after = [a for a in run.kc.host_arrays() if a is not None]
+    for a, b in zip(before, after):
+        np.testing.assert_array_equal(a, b)
+    # a decode range past the capacity is clipped and flagged
+    run.s.status.zero_()
+    run.decode(lens=np.array([1, 1, 64]), starts=np.array([0, 0, run.cap - 32]))
+    assert run.status() & 4
+
+
+def test_determinism():
+    w = W.WORKLOADS[2]
+    run = Run(w, batch=1, n_tokens=512)
+    run.quantize()
+    a = [x.copy() for c in run.host_caches() for x in c if x is not None]
+    o1 = run.decode()
+    run.kc.idx.zero_(); run.vc.idx.zero_()
+    run.quantize()
+    b = [x for c in run.host_caches() for x in c if x is not None]
+    o2 = run.decode()
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    np.testing.assert_array_equal(o1, o2)
+
+
+# ------------------------------------------------- full-size, sampled checks ---
+@pytest.mark.parametrize("wid", [2, 3, 5])
+def test_full_workload_sampled(wid):
+    w = W.WORKLOADS[wid]
+    _log(f"workload {wid} full: generating inputs")
+    run = Run(w)
+    _log(f"workload {wid} full: quantize {run.batch}x{w.n_kv_heads}x{run.T}")
+    dbg = run.quantize()
+    check_quantize(run, dbg, samples=wid, label=f"w{wid}-full")
+    _log(f"workload {wid} full: decode")
+    out = run.decode()
+    rng = np.random.default_rng(wid)
+    pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, run.batch, 2), rng.integers(0, w.n_kv_heads, 2))]
+    check_decode(run, out, pairs=pairs, label=f"w{wid}-full")
+    assert run.status() == 0
+
+
+def test_full_workload4_ragged_sampled():
+    w = W.WORKLOADS[4]
+    lens = W.seq_lengths(w)
+    _log("workload 4 full: generating inputs")
+    run = Run(w, lens=lens, extra=1)
+    _log("workload 4 full: prefill quantize (setup), one call per sequence")
+    for s in range(w.batch):
+        run.quantize(K=run.K[s:s + 1, :, :lens[s]], V=run.V[s:s + 1, :, :lens[s]], dst=run.starts[s:s + 1])
+    newk = np.stack([np.stack([W.new_tokens(w, 0, s, h) for h in range(w.n_kv_heads)]) for s in range(w.batch)])
+    newv = np.stack([np.stack([W.new_tokens(w, 1, s, h) for h in range(w.n_kv_heads)]) for s in range(w.batch)])
+    dst = run.starts + lens
+    _log("workload 4 full: incremental quantize")
+    dbg = run.quantize(K=newk, V=newv, dst=dst)
+    check_quantize(run, dbg, K=newk, V=newv, starts=dst, label="w4-incremental")
+    for s in range(w.batch):
+        run.K[s, :, lens[s]] = newk[s, :, 0]
+        run.V[s, :, lens[s]] = newv[s, :, 0]
+    lens1 = lens + 1
+    out = run.decode(lens=lens1)
+    rng = np.random.default_rng(4)
+    pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, w.batch, 3), rng.integers(0, w.n_kv_heads, 3))]
+    check_decode(run, out, pairs=pairs, lens=lens1, label="w4-full")

@@ -190,3 +190,25 @@ def capacity(lens: np.ndarray, align: int = 64) -> int:
 def small(w: Workload, **kw) -> Workload:
     """A reduced copy of a workload (same value model and bits) for fast tests."""
     return dataclasses.replace(w, **kw)
+
+
+def kv_batch(w: Workload, tensor: int, n_tokens: Optional[int] = None, batch: Optional[int] = None,
+             threads: int = 8) -> np.ndarray:
+    """Stored K or V of the whole batch: [batch][n_kv_heads][n_tokens][d] (storage dtype).
+
+    Chunks are independent streams, drawn in parallel threads.
+    """
+    import concurrent.futures as cf
+    nb = w.batch if batch is None else batch
+    n = w.seq_len if n_tokens is None else n_tokens
+    dt = np.float32 if w.dtype == "f32" else np.uint16
+    out = np.empty((nb, w.n_kv_heads, n, w.d), dtype=dt)
+
+    def one(job):
+        s, h = job
+        out[s, h] = kv_chunk(w, tensor, s, h, n_tokens=n)
+
+    jobs = [(s, h) for s in range(nb) for h in range(w.n_kv_heads)]
+    with cf.ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(one, jobs))
+    return out
