@@ -57,7 +57,7 @@ class Run:
         self.kc, self.vc = self.s.new_caches(self.cap)
         self.K = W.kv_batch(w, 0, n_tokens=self.T + extra, batch=self.batch)
         self.V = W.kv_batch(w, 1, n_tokens=self.T + extra, batch=self.batch)
-        self.Q = W.queries(w)[: self.batch]
+        self.Q = W.queries(W.small(w, batch=self.batch))
 
     def dev(self, a):
         t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
