@@ -23,11 +23,13 @@ LIB = os.path.join(PKG, "libtq.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-SOURCES = ["tq_host.cpp", "tq_plain.hip"]
+SOURCES = ["tq_host.cpp", "tq_plain.hip", "tq_decode_fast.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
+          f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function",
+          # keep MFMA accumulators in ordinary VGPRs (no AGPR copies around them)
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:

@@ -42,9 +42,11 @@ inline PrepLayout prep_layout(int d, int m) {
 // Token splits of the decode partial pass.  The same plan sizes the workspace
 // and the launch, so both derive it from (batch, kv heads, max_len) alone.
 struct DecodePlan {
-  int32_t split_tokens;  // tokens per split, a multiple of 64
-  int32_t n_split;       // splits per (sequence, kv head)
-  size_t off_qr, off_qs, off_part, total;  // workspace byte offsets
+  int32_t split_tokens;  // tokens per split, a multiple of 256
+  int32_t n_split;       // splits per (sequence, kv head), covering max_len + 63 slots
+  int32_t fast;          // 1: matrix-core kernels; 0: reference-grade kernels
+  int32_t rb;            // row blocks of 16 (= G / 4) in the matrix-core kernels
+  size_t off_qr, off_qs, off_part, off_qop, off_qconst, total;  // workspace byte offsets
   int32_t part_stride;   // floats per partial record: 2 + d + m
 };
 
@@ -92,6 +94,10 @@ struct DecodeTensorArgs {
 
 struct DecodeArgs {
   DecodeTensorArgs k, v;
+  double walsh_k[4];     // key codebook Walsh coefficients, planes ordered s0, s1, s2, s0 s1 s2
+  double walsh_v[4];     // value codebook, same order
+  void *qop;             // matrix-core A operands of the queries (fast path)
+  double *qconst;        // [batch][Hq][4]: idx correction, sign correction, alpha, beta
   const void *q;         // [batch][Hq][d]
   int32_t dtype;
   int32_t batch, Hkv, Hq, G;
@@ -114,5 +120,6 @@ struct DecodeArgs {
 // Host launchers (defined in the .hip translation units).  Return hipError_t.
 int launch_quantize(int d, const QuantArgs &a, hipStream_t s);
 int launch_decode(int d, const DecodeArgs &a, hipStream_t s);
+int launch_decode_fast(int d, int rb, const DecodeArgs &a, hipStream_t s);
 
 }  // namespace tq

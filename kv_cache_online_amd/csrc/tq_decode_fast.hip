@@ -1,0 +1,731 @@
+// Decode attention over the packed caches on the CDNA4 matrix cores.
+//
+// The speed of decode over a compressed cache comes from moving fewer bytes
+// (ast-softpro.ru, "Технология TurboQuant и её применение с локальными LLM",
+// section 1.3).  On MI355X the vector ALU cannot keep up with HBM if every
+// query head takes its own dot products with every unpacked coordinate, so the
+// contractions of all G query heads of a kv head run as exact integer MFMAs
+// (v_mfma_i32_16x16x64_i8):
+//
+//  * Bit-plane operands.  A codebook value is an odd function of the +-1
+//    bit-planes of its index (Walsh expansion: b' = 1, 2 are linear, b' = 3 adds
+//    the triple product s0 s1 s2 = 2 (b0 ^ b1 ^ b2) - 1).  With s = 2 b - 1 a
+//    dot product with a plane is 2 <v, b> - sum(v), so the MFMA only needs 0/1
+//    bits.  A packed word (shifted right by 4 for the odd nibbles) ANDed with
+//    0x01010101 << k yields four int8 operand bytes bit << k, k = 0..3; the
+//    other operand is pre-divided by 2^k.
+//  * Fixed-point slices.  Each real operand v (Walsh-weighted rotated query,
+//    sketched query, softmax weight times scale) becomes F = rint(v 2^E) with
+//    |F| < 2^30, written as four signed base-256 digits (bytes of
+//    (F + 0x808080) ^ 0x808080).  Rows of the MFMA are (query head, digit), so
+//    16 rows hold 4 heads; G = 8 uses two row blocks.  Digit sums are recombined
+//    exactly in float64.
+//  * Exact split maximum.  Scores of a split (at most 8192 / G slots) are kept in
+//    LDS; the value pass runs after the split's maximum is known, so the integer
+//    accumulators never need rescaling.
+//
+// Keys are read token-major (a token's planes contiguous: the score contraction
+// runs over coordinates); values in the 32-slot transposed layout (a word holds
+// one coordinate of 32 consecutive slots: the value contraction runs over
+// tokens).  Splits are aligned to absolute 64-slot tiles.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "tq_common.h"
+
+namespace tq {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kSigPlane = 4;     // operand / accumulator slot of the sign plane
+constexpr int kScoreFloats = 8192;
+
+__device__ inline int n_walsh(int bq) { return bq == 3 ? 4 : bq; }
+
+__device__ inline float load_q(const void *x, int dtype, size_t i) {
+  if (dtype == TQ_BF16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(x)[i]) << 16);
+  return static_cast<const float *>(x)[i];
+}
+
+__device__ inline float f16v(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu)));
+}
+
+__device__ inline v4i expand(uint32_t w, uint32_t sh, const uint32_t (&m)[4]) {
+  w >>= sh;
+  v4i r;
+  r.x = static_cast<int>(w & m[0]);
+  r.y = static_cast<int>(w & m[1]);
+  r.z = static_cast<int>(w & m[2]);
+  r.w = static_cast<int>(w & m[3]);
+  return r;
+}
+
+// Word of Walsh plane p (p < 3: index bit-plane p; p == 3: b0 ^ b1 ^ b2, whose
+// +-1 form is the triple product s0 s1 s2).
+template <int PM>
+__device__ inline uint32_t plane_word(int p, uint32_t w0, uint32_t w1, uint32_t w2) {
+  return p == 0 ? w0 : p == 1 ? w1 : p == 2 ? w2 : (w0 ^ w1 ^ w2);
+}
+
+// N consecutive 32-bit words (N = 2 or 4), one vector load.
+template <int N>
+__device__ inline void load_words(const uint32_t *p, uint32_t (&o)[N]) {
+  if constexpr (N == 2) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    o[0] = v.x;
+    o[1] = v.y;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
+  }
+}
+
+// N consecutive 32-bit words through a buffer descriptor (0 past its end).
+template <int N>
+__device__ inline void buf_words(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t (&o)[N]) {
+  typedef unsigned u2 __attribute__((ext_vector_type(2)));
+  typedef unsigned u4 __attribute__((ext_vector_type(4)));
+  if constexpr (N == 2) {
+    const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    o[0] = v.x;
+    o[1] = v.y;
+  } else {
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
+  }
+}
+
+__device__ inline v4i mfma(v4i a, v4i b, v4i c) { return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0); }
+
+// sum_l 256^l c_l, exact: every digit sum is below 2^21 in magnitude (operand
+// bytes <= 8, digits <= 128, at most 2048 terms), so pairs combine in int32.
+__device__ inline double combine(v4i c) {
+  const int32_t lo = c.x + (c.y << 8), hi = c.z + (c.w << 8);
+  return fma(static_cast<double>(hi), 65536.0, static_cast<double>(lo));
+}
+
+// The +-1 form sum_t w_t (2 b_t - 1) from digit sums x of weight x bit and k of
+// weight x 1: 2 x_l - k_l per digit (each below 2^23), then recombined.
+__device__ inline double pm_form(v4i x, v4i k) {
+  const v4i r = {2 * x.x - k.x, 2 * x.y - k.y, 2 * x.z - k.z, 2 * x.w - k.w};
+  const int32_t lo = r.x + (r.y << 8), hi = r.z + (r.w << 8);
+  return fma(static_cast<double>(hi), 65536.0, static_cast<double>(lo));
+}
+
+__device__ inline uint32_t digits(int32_t f) { return static_cast<uint32_t>(f + 0x00808080) ^ 0x00808080u; }
+
+// Exponent E with vmax * 2^E < 2^30 (0 for vmax == 0).
+__device__ inline int fix_exp(double vmax) { return vmax > 0.0 ? 29 - ilogb(vmax) : 0; }
+
+__device__ inline void clip_seq(const DecodeArgs &a, int b, int64_t *start, int64_t *len) {
+  int64_t s = a.seq_start[b], n = a.seq_len[b];
+  const int64_t cap = a.k.cap < a.v.cap ? a.k.cap : a.v.cap;
+  bool bad = false;
+  if (n < 0) { n = 0; bad = true; }
+  if (s < 0 || s > cap) { s = 0; n = 0; bad = true; }
+  if (s + n > cap) { n = cap - s; bad = true; }
+  if (bad && a.status && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicOr(a.status, TQ_FLAG_OUT_OF_RANGE);
+  *start = s;
+  *len = n;
+}
+
+// ------------------------------------------------------------- query prep ---
+// One block per (sequence, query head): q_rot = Pi q and q_s = S q in float64,
+// then this head's four rows (one per digit) of every score operand, written
+// as 16-byte lane entries, and the exact correction constants
+// sum_j F_j 2^shift_j.
+template <int D>
+__global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
+  constexpr int C = D / 64;
+  __shared__ double q[D], qr[D], qs[D];
+  __shared__ double red[2][256];
+  __shared__ double pj[256 / (D / 4)][2][D];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x, b = bh / a.Hq, hq = bh % a.Hq;
+  const int kvh = hq / a.G, hl = hq % a.G, rb = hl >> 2, row0 = (hl & 3) * 4;
+  const int RB = a.G / 4;
+  for (int j = tid; j < D; j += 256) q[j] = load_q(a.q, a.dtype, size_t(bh) * D + j);
+  __syncthreads();
+  // q_rot[j] = sum_k Pi[j][k] q[k] (rows of Pi^T), q_s likewise with S^T:
+  // thread (kg, jg) sums rows k of its k range for 4 consecutive columns
+  {
+    constexpr int JG = D / 4, KG = 256 / JG, KPER = D / KG;
+    const int jg = tid % JG, kg = tid / JG;
+    double xr[4] = {0.0, 0.0, 0.0, 0.0}, xs[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+    for (int kk = 0; kk < KPER; ++kk) {
+      const int k = kg * KPER + kk;
+      const float4 r = *reinterpret_cast<const float4 *>(a.rotT + size_t(k) * D + 4 * jg);
+      const float4 t = *reinterpret_cast<const float4 *>(a.projT + size_t(k) * D + 4 * jg);
+      const double qk = q[k];
+      xr[0] = fma(double(r.x), qk, xr[0]);
+      xr[1] = fma(double(r.y), qk, xr[1]);
+      xr[2] = fma(double(r.z), qk, xr[2]);
+      xr[3] = fma(double(r.w), qk, xr[3]);
+      xs[0] = fma(double(t.x), qk, xs[0]);
+      xs[1] = fma(double(t.y), qk, xs[1]);
+      xs[2] = fma(double(t.z), qk, xs[2]);
+      xs[3] = fma(double(t.w), qk, xs[3]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      pj[kg][0][4 * jg + u] = xr[u];
+      pj[kg][1][4 * jg + u] = xs[u];
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < D; j += 256) {
+    constexpr int KG = 256 / (D / 4);
+    double vr = 0.0, vs = 0.0;
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      vr += pj[g][0][j];
+      vs += pj[g][1][j];
+    }
+    qr[j] = vr;
+    qs[j] = vs;
+  }
+  __syncthreads();
+  const int npk = n_walsh(a.k.bq);
+  double amax = 0.0;
+  for (int p = 0; p < npk; ++p) amax = fmax(amax, fabs(a.walsh_k[p]));
+  double mr = 0.0, ms = 0.0;
+  for (int j = tid; j < D; j += 256) {
+    mr = fmax(mr, fabs(qr[j]));
+    ms = fmax(ms, fabs(qs[j]));
+  }
+  red[0][tid] = mr;
+  red[1][tid] = ms;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      red[0][tid] = fmax(red[0][tid], red[0][tid + o]);
+      red[1][tid] = fmax(red[1][tid], red[1][tid + o]);
+    }
+    __syncthreads();
+  }
+  const int Ei = fix_exp(amax * red[0][0]), Es = fix_exp(red[1][0]);
+  __syncthreads();
+  uint4 *op = reinterpret_cast<uint4 *>(static_cast<unsigned char *>(a.qop) +
+                                        (size_t(b * a.Hkv + kvh) * RB + rb) * 5 * C * kWave * 16);
+  const int nplane = npk + a.k.sketch;
+  double ki = 0.0, ks = 0.0;
+  // entry = (plane, chunk c, lane group g, digit l): 16 bytes for VGPR s, byte i
+  for (int e = tid; e < nplane * C * 16; e += 256) {
+    const int l = e & 3, g = (e >> 2) & 3, c = (e >> 4) % C, pidx = (e >> 4) / C;
+    const bool sign = pidx == npk;
+    uint32_t wv[4] = {0u, 0u, 0u, 0u};
+    double ksum = 0.0;
+#pragma unroll
+    for (int sv = 0; sv < 4; ++sv)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int par = g & 1;
+        const int j = 32 * ((g >> 1) * C + c) + 8 * i + sv + 4 * par;
+        const double v = sign ? qs[j] : a.walsh_k[pidx] * qr[j];
+        const double F = rint(ldexp(v, (sign ? Es : Ei) - sv));
+        ksum += ldexp(F, sv);
+        const uint32_t dg = digits(static_cast<int32_t>(F));
+        wv[sv] |= ((dg >> (8 * l)) & 0xFFu) << (8 * i);
+      }
+    if (l == 0) {
+      if (sign) ks += ksum;
+      else ki += ksum;
+    }
+    const int slot = sign ? kSigPlane : pidx;
+    op[(size_t(slot) * C + c) * kWave + 16 * g + row0 + l] = uint4{wv[0], wv[1], wv[2], wv[3]};
+  }
+  red[0][tid] = ki;
+  red[1][tid] = ks;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      red[0][tid] += red[0][tid + o];
+      red[1][tid] += red[1][tid + o];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const double base = double(a.sm_scale) * 1.4426950408889634;  // log2(e): scores in base 2
+    a.qconst[size_t(bh) * 4 + 0] = red[0][0];
+    a.qconst[size_t(bh) * 4 + 1] = red[1][0];
+    a.qconst[size_t(bh) * 4 + 2] = ldexp(base, -Ei);
+    a.qconst[size_t(bh) * 4 + 3] = ldexp(base * double(a.kappa), -Es);
+  }
+}
+
+// ------------------------------------------------------------ split pass ---
+// One 256-thread block per (split, kv head, sequence).  BQK / BQV: index bits
+// of keys / values (compile time: the plane loops unroll without branches);
+// the sign planes always run, with zero operands when a tensor has no sketch.
+//
+// Lane roles: lane = 16 grp + col.  In a score MFMA col is the token of a
+// 16-token block and grp the lane group of the contraction (coordinates); the
+// result gives lane (col, grp) the four digit sums of query head 4 rb + grp
+// for that token.  In a value MFMA col is the coordinate of a 16-coordinate
+// block and grp the token group of the contraction.
+//
+// Loads are raw buffer loads: a per-split descriptor (SGPRs) whose size stops
+// at the cache capacity (reads past it return 0), a per-lane constant VGPR
+// offset and a wave-uniform SGPR offset per tile.
+template <int D, int RB, int BQK, int BQV>
+__global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
+  constexpr int C = D / 64, W = D / 32, NB = D / 64, G = 4 * RB;
+  constexpr int PK = BQK == 3 ? 4 : BQK, PV = BQV == 3 ? 4 : BQV;
+  const int SMAX = a.split_tokens;
+  constexpr int KREC = BQK * W * 4, KSREC = W * 4;      // key bytes per slot: planes, signs
+  constexpr int VREC = BQV * D * 4, VSREC = D * 4;      // value bytes per 32-slot block
+  constexpr uint32_t kDword3 = 0x00020000u;             // raw buffer, 32-bit data format (gfx9)
+  extern __shared__ float sc[];                              // [head][slot in split], base-2 units (S x G)
+  __shared__ __attribute__((aligned(16))) unsigned char aw[2][4][4][RB][16][16];  // [part][tile][kgroup][rb][row][byte]
+  __shared__ float redf[4][G];
+  __shared__ float redv[4][2];
+  __shared__ float mh_s[G];
+  __shared__ float lh_s[G];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int64_t start, len;
+  clip_seq(a, b, &start, &len);
+  const int S = a.split_tokens;
+  const int64_t abase = (start & ~int64_t(63)) + int64_t(split) * S;
+  const int64_t lo = abase > start ? abase : start;
+  const int64_t hi = (abase + S) < (start + len) ? (abase + S) : (start + len);
+  const int bh0 = b * a.Hq + h * G;
+  const int stride = 2 + 2 * D;
+  if (lo >= hi) {
+    if (tid < G) {
+      float *o = a.part + (size_t(bh0 + tid) * a.n_split + split) * stride;
+      o[0] = -INFINITY;
+      o[1] = 0.0f;
+    }
+    return;
+  }
+  const int ntile = static_cast<int>((hi - abase + 63) >> 6);
+  const int vlo = static_cast<int>(lo - abase), vhi = static_cast<int>(hi - abase);  // valid slots
+  const uint32_t sh = (grp & 1) ? 4u : 0u;           // odd nibbles: shift the word right by 4
+  const uint32_t msk[4] = {0x01010101u, 0x02020202u, 0x04040404u, 0x08080808u};
+  const int64_t kcap = a.k.cap, vcap = a.v.cap, vblocks = vcap >> 5;
+  const bool skk = a.k.sketch != 0, skv = a.v.sketch != 0;
+  const int kslots = static_cast<int>((kcap - abase) < S ? (kcap - abase) : S);
+  const int64_t blk0 = abase >> 5;
+  const int vblk = static_cast<int>((vblocks - blk0) < (S >> 5) ? (vblocks - blk0) : (S >> 5));
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(a.k.idx + (int64_t(h) * kcap + abase) * BQK * W), 0, kslots * KREC, kDword3);
+  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(skk ? a.k.sgn + (int64_t(h) * kcap + abase) * W : a.k.idx), 0,
+      skk ? kslots * KSREC : 0, kDword3);
+  const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.k.scl + (int64_t(h) * kcap + abase) * 2), 0, kslots * 4, kDword3);
+  const int vslots = static_cast<int>((vcap - abase) < S ? (vcap - abase) : S);
+  const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.v.scl + (int64_t(h) * vcap + abase) * 2), 0, vslots * 4, kDword3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(a.v.idx + (int64_t(h) * vblocks + blk0) * BQV * D), 0, vblk * VREC, kDword3);
+  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(skv ? a.v.sgn + (int64_t(h) * vblocks + blk0) * D : a.v.idx), 0,
+      skv ? vblk * VSREC : 0, kDword3);
+
+  // ---- loads: one key tile and one value round per register buffer ----
+  const int kvo = col * KREC + (grp >> 1) * C * 4, ksvo = col * KSREC + (grp >> 1) * C * 4;
+  const int j0 = wave * (D / 4) + col * NB;
+  const int vvo = (grp >> 1) * VREC + j0 * 4, vsvo = (grp >> 1) * VSREC + j0 * 4;
+  auto load_k = [&](uint32_t (&wd)[4][3][C], uint32_t (&ws)[4][C], uint32_t (&ksc)[4], uint32_t (&vsc)[4],
+                    int tile) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int t0 = tile * 64 + nb * 16;  // wave-uniform
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        if (p < BQK) buf_words<C>(rk, kvo + p * W * 4, t0 * KREC, wd[nb][p]);
+        else
+#pragma unroll
+          for (int c = 0; c < C; ++c) wd[nb][p][c] = 0u;
+      }
+      buf_words<C>(rks, ksvo, t0 * KSREC, ws[nb]);
+      ksc[nb] = __builtin_amdgcn_raw_buffer_load_b32(rkc, col * 4, t0 * 4, 0);
+      vsc[nb] = __builtin_amdgcn_raw_buffer_load_b32(rvc, col * 4, t0 * 4, 0);
+    }
+  };
+  // value words of this wave's coordinates for the round's 4 tiles, and the
+  // value scales of the wave's own tile of the round
+  auto load_v = [&](uint32_t (&vw)[4][3][NB], uint32_t (&vs)[4][NB], uint32_t (&vsc)[4], int r) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int bl = 2 * (4 * r + tt);  // first 32-slot block of the tile
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        if (p < BQV) buf_words<NB>(rv, vvo + p * D * 4, bl * VREC, vw[tt][p]);
+        else
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) vw[tt][p][nb] = 0u;
+      }
+      buf_words<NB>(rvs, vsvo, bl * VSREC, vs[tt]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      vsc[nb] = __builtin_amdgcn_raw_buffer_load_b32(rvc, col * 4, ((4 * r + wave) * 64 + nb * 16) * 4, 0);
+  };
+
+  uint32_t ka_wd[4][3][C], ka_ws[4][C], ka_ksc[4], ka_vsc[4];
+  uint32_t va_w[4][3][NB], va_s[4][NB], va_sc[4];
+  const int nround = (ntile + 3) >> 2;
+  load_k(ka_wd, ka_ws, ka_ksc, ka_vsc, wave);   // past the tiles: the descriptor returns 0
+  load_v(va_w, va_s, va_sc, 0);
+
+  // ---- phase 1: scores of this wave's tiles ----
+  v4i qa[RB][PK + 1][C];
+  double kci[RB], kcs[RB];
+  float al[RB], be[RB];
+  {
+    const v4i *qop = static_cast<const v4i *>(a.qop) + size_t(b * a.Hkv + h) * RB * 5 * C * kWave;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int p = 0; p <= PK; ++p) {
+        const int slot = p == PK ? kSigPlane : p;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          qa[rb][p][c] = (p < PK || skk) ? qop[((size_t(rb) * 5 + slot) * C + c) * kWave + lane] : v4i{0, 0, 0, 0};
+      }
+      const double *qc = a.qconst + size_t(bh0 + rb * 4 + grp) * 4;
+      kci[rb] = qc[0];
+      kcs[rb] = skk ? qc[1] : 0.0;
+      al[rb] = static_cast<float>(qc[2]);
+      be[rb] = skk ? static_cast<float>(qc[3]) : 0.0f;
+    }
+  }
+  float mloc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) mloc[rb] = -INFINITY;
+  float vnumax = 0.0f, vrhomax = 0.0f;
+  auto score_k = [&](const uint32_t (&wd)[4][3][C], const uint32_t (&ws)[4][C], const uint32_t (&ksc)[4],
+                     const uint32_t (&vsc)[4], int tile) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int t = tile * 64 + nb * 16 + col;
+      const bool valid = t >= vlo && t < vhi;
+      v4i acc_i[RB], acc_s[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc_i[rb] = acc_s[rb] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+#pragma unroll
+        for (int p = 0; p < PK; ++p) {
+          const v4i B = expand(plane_word<4>(p, wd[nb][0][c], wd[nb][1][c], wd[nb][2][c]), sh, msk);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc_i[rb] = mfma(qa[rb][p][c], B, acc_i[rb]);
+        }
+        const v4i B = expand(ws[nb][c], sh, msk);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc_s[rb] = mfma(qa[rb][PK][c], B, acc_s[rb]);
+      }
+      const float knu = f16v(ksc[nb]), krho = f16v(ksc[nb] >> 16);
+      vnumax = fmaxf(vnumax, valid ? f16v(vsc[nb]) : 0.0f);
+      vrhomax = fmaxf(vrhomax, valid ? f16v(vsc[nb] >> 16) : 0.0f);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float ri = static_cast<float>(fma(2.0, combine(acc_i[rb]), -kci[rb]));
+        const float rs = static_cast<float>(fma(2.0, combine(acc_s[rb]), -kcs[rb]));
+        float sv = fmaf(knu * al[rb], ri, (krho * be[rb]) * rs);
+        sv = valid ? sv : -INFINITY;
+        sc[(rb * 4 + grp) * SMAX + t] = sv;
+        mloc[rb] = fmaxf(mloc[rb], sv);
+      }
+    }
+  };
+  for (int tile = wave; tile < ntile; tile += 4) {
+    if (tile != wave) load_k(ka_wd, ka_ws, ka_ksc, ka_vsc, tile);
+    score_k(ka_wd, ka_ws, ka_ksc, ka_vsc, tile);
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) mloc[rb] = fmaxf(mloc[rb], __shfl_xor(mloc[rb], o, kWave));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    vnumax = fmaxf(vnumax, __shfl_xor(vnumax, o, kWave));
+    vrhomax = fmaxf(vrhomax, __shfl_xor(vrhomax, o, kWave));
+  }
+  if (col == 0)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) redf[wave][rb * 4 + grp] = mloc[rb];
+  if (lane == 0) {
+    redv[wave][0] = vnumax;
+    redv[wave][1] = vrhomax;
+  }
+  __syncthreads();
+  if (tid < G) mh_s[tid] = fmaxf(fmaxf(redf[0][tid], redf[1][tid]), fmaxf(redf[2][tid], redf[3][tid]));
+  const float vn_all = fmaxf(fmaxf(redv[0][0], redv[1][0]), fmaxf(redv[2][0], redv[3][0]));
+  const float vr_all = fmaxf(fmaxf(redv[0][1], redv[1][1]), fmaxf(redv[2][1], redv[3][1]));
+  const int Ew = fix_exp(vn_all), Ewp = fix_exp(vr_all);
+  __syncthreads();
+  float mh[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) mh[rb] = mh_s[rb * 4 + grp];
+
+  // ---- phase 2: per round of 4 tiles, weights to digits, then value MFMAs ----
+  // av[p] accumulates digit sums of weight x bit-plane p (slot PV: sign plane,
+  // residual weights); ak[part] accumulates weight x 1 (the all-ones plane),
+  // which the +-1 form of every plane needs.  Every wave runs every tile of a
+  // round, so each wave's ak is complete.
+  v4i av[PV + 1][NB][RB], ak[2][RB];
+#pragma unroll
+  for (int p = 0; p <= PV; ++p)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) av[p][nb][rb] = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) ak[0][rb] = ak[1][rb] = v4i{0, 0, 0, 0};
+  const v4i ones = {static_cast<int>(msk[0]), static_cast<int>(msk[1]), static_cast<int>(msk[2]),
+                    static_cast<int>(msk[3])};
+  float lloc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) lloc[rb] = 0.0f;
+  auto value_round = [&](const uint32_t (&vw)[4][3][NB], const uint32_t (&vs)[4][NB], const uint32_t (&vsc)[4],
+                         int r) {
+    const int tile = 4 * r + wave;
+    if (tile < ntile) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int w64 = nb * 16 + col, t = tile * 64 + w64;
+        const bool valid = t >= vlo && t < vhi;
+        const float vnu = valid ? f16v(vsc[nb]) : 0.0f, vrho = valid ? f16v(vsc[nb] >> 16) : 0.0f;
+        // token w64 of the tile: 32-slot block w64 >> 5, nibble (w64 & 31) >> 2,
+        // bit w64 & 3 of the nibble -> token group q, operand byte pos, shift
+        const int within = w64 & 31, nib = within >> 2, sft = within & 3;
+        const int q = 2 * (w64 >> 5) + (nib & 1), pos = 4 * sft + (nib >> 1);
+        const float sw = ldexpf(vnu, Ew - sft), swp = ldexpf(vrho, Ewp - sft);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int head = rb * 4 + grp;
+          const float P = valid ? exp2f(sc[head * SMAX + t] - mh[rb]) : 0.0f;
+          lloc[rb] += P;
+          // truncation toward zero: |error| < 1 unit of 2^-Ew, far below the
+          // 24-bit resolution of the float weight itself
+          const uint32_t dw = digits(static_cast<int32_t>(P * sw));
+          const uint32_t dp = digits(static_cast<int32_t>(P * swp));
+#pragma unroll
+          for (int l = 0; l < 4; ++l) {
+            aw[0][tile & 3][q][rb][grp * 4 + l][pos] = static_cast<unsigned char>(dw >> (8 * l));
+            aw[1][tile & 3][q][rb][grp * 4 + l][pos] = static_cast<unsigned char>(dp >> (8 * l));
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if (4 * r + tt >= ntile) break;
+      v4i aw0[RB], aw1[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        aw0[rb] = *reinterpret_cast<const v4i *>(&aw[0][tt][grp][rb][col][0]);
+        aw1[rb] = *reinterpret_cast<const v4i *>(&aw[1][tt][grp][rb][col][0]);
+        ak[0][rb] = mfma(aw0[rb], ones, ak[0][rb]);
+        ak[1][rb] = mfma(aw1[rb], ones, ak[1][rb]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int p = 0; p < PV; ++p) {
+          const v4i B = expand(plane_word<4>(p, vw[tt][0][nb], vw[tt][1][nb], vw[tt][2][nb]), sh, msk);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) av[p][nb][rb] = mfma(aw0[rb], B, av[p][nb][rb]);
+        }
+        const v4i B = expand(vs[tt][nb], sh, msk);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) av[PV][nb][rb] = mfma(aw1[rb], B, av[PV][nb][rb]);
+      }
+    }
+    __syncthreads();
+  };
+  for (int r = 0; r < nround; ++r) {
+    if (r > 0) load_v(va_w, va_s, va_sc, r);
+    value_round(va_w, va_s, va_sc, r);
+  }
+
+  // ---- l over the block, then write this split's partial ----
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) lloc[rb] += __shfl_xor(lloc[rb], o, kWave);
+  if (col == 0)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) redf[wave][rb * 4 + grp] = lloc[rb];
+  __syncthreads();
+  if (tid < G) lh_s[tid] = (redf[0][tid] + redf[1][tid]) + (redf[2][tid] + redf[3][tid]);
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int head = rb * 4 + grp;
+    float *o = a.part + (size_t(bh0 + head) * a.n_split + split) * stride;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      double acc = 0.0;
+#pragma unroll
+      for (int p = 0; p < PV; ++p) acc += a.walsh_v[p] * pm_form(av[p][nb][rb], ak[0][rb]);
+      o[2 + j0 + nb] = static_cast<float>(ldexp(acc, -Ew));
+      o[2 + D + j0 + nb] = skv ? static_cast<float>(ldexp(pm_form(av[PV][nb][rb], ak[1][rb]), -Ewp)) : 0.0f;
+    }
+    if (wave == 0 && col == 0) {
+      o[0] = mh[rb] * 0.69314718055994531f;  // natural-log units for the merge
+      o[1] = lh_s[head];
+    }
+  }
+}
+
+// ----------------------------------------------------------------- merge ---
+// One block per (sequence, query head): log-sum-exp merge of the split
+// partials, then out = (Pi^T A + kappa S^T B) / l.
+// Thread (sg, eg), sg = tid / 16, eg = tid % 16, sums splits sg, sg + 16, ...
+// for the EPT consecutive elements eg * EPT of (A, B) with vector loads, so
+// many loads are in flight; the 16 split groups are then reduced in LDS.  A
+// split with no tokens has weight 0 and unwritten A, B, which are masked.
+// The projection tiles k across 256 / (D / 4) thread groups (float4 columns).
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_fast(DecodeArgs a) {
+  constexpr int EPT = 2 * D / 16;                 // elements of (A, B) per thread
+  constexpr int JG = D / 4, KG = 256 / JG, KPER = D / KG;
+  __shared__ float red[256];
+  __shared__ __attribute__((aligned(16))) float part_s[16][2 * D];
+  __shared__ __attribute__((aligned(16))) float AB[2 * D];
+  __shared__ __attribute__((aligned(16))) float prj[KG][D];
+  const int tid = threadIdx.x, sg = tid >> 4, eg = tid & 15;
+  const size_t bh = blockIdx.x;
+  const int stride = 2 + 2 * D, ns = a.n_split;
+  const float *base = a.part + bh * ns * stride;
+  float M = -INFINITY;
+  for (int s = tid; s < ns; s += 256)
+    if (base[size_t(s) * stride + 1] > 0.0f) M = fmaxf(M, base[size_t(s) * stride]);
+  red[tid] = M;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  M = red[0];
+  __syncthreads();
+  float acc[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] = 0.0f;
+  float lpart = 0.0f;
+  for (int s = sg; s < ns; s += 16) {
+    const float *p = base + size_t(s) * stride;
+    const float l = p[1];
+    const float w = l > 0.0f ? expf(p[0] - M) : 0.0f;
+    if (eg == 0) lpart = fmaf(w, l > 0.0f ? l : 0.0f, lpart);
+    // partial records are 2 + 2D floats: element 2 + e sits 8 bytes past a
+    // 16-byte boundary, so read as float2 pairs
+    const float2 *q = reinterpret_cast<const float2 *>(p + 2 + eg * EPT);
+#pragma unroll
+    for (int e = 0; e < EPT / 2; ++e) {
+      const float2 x = q[e];
+      acc[2 * e] = fmaf(w, w != 0.0f ? x.x : 0.0f, acc[2 * e]);
+      acc[2 * e + 1] = fmaf(w, w != 0.0f ? x.y : 0.0f, acc[2 * e + 1]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) part_s[sg][eg * EPT + e] = acc[e];
+  red[tid] = lpart;
+  __syncthreads();
+  for (int e = tid; e < 2 * D; e += 256) {
+    float v = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) v += part_s[g][e];
+    AB[e] = v;
+  }
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const float l = red[0];
+  // projection: thread (kg, jg) sums rows k in [kg * KPER, (kg + 1) * KPER) for
+  // output columns 4 jg .. 4 jg + 3
+  {
+    const int jg = tid % JG, kg = tid / JG;
+    float4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+    for (int kk = 0; kk < KPER; ++kk) {
+      const int k = kg * KPER + kk;
+      const float4 r = *reinterpret_cast<const float4 *>(a.rot + size_t(k) * D + 4 * jg);
+      const float av = AB[k];
+      x.x = fmaf(r.x, av, x.x);
+      x.y = fmaf(r.y, av, x.y);
+      x.z = fmaf(r.z, av, x.z);
+      x.w = fmaf(r.w, av, x.w);
+      if (a.v.sketch) {
+        const float4 sp = *reinterpret_cast<const float4 *>(a.proj + size_t(k) * D + 4 * jg);
+        const float bv = a.kappa * AB[D + k];
+        x.x = fmaf(sp.x, bv, x.x);
+        x.y = fmaf(sp.y, bv, x.y);
+        x.z = fmaf(sp.z, bv, x.z);
+        x.w = fmaf(sp.w, bv, x.w);
+      }
+    }
+    *reinterpret_cast<float4 *>(&prj[kg][4 * jg]) = x;
+  }
+  __syncthreads();
+  for (int j = tid; j < D; j += 256) {
+    float o = 0.0f;
+#pragma unroll
+    for (int g = 0; g < KG; ++g) o += prj[g][j];
+    a.out[bh * D + j] = l > 0.0f ? o / l : 0.0f;
+  }
+}
+
+template <int D, int RB, int BQK>
+int launch_partial_bv(int bqv, const DecodeArgs &a, hipStream_t s) {
+  const dim3 grid(a.n_split, a.Hkv, a.batch);
+  const size_t lds = size_t(a.split_tokens) * 4 * RB * sizeof(float);  // scores: split x G
+  switch (bqv) {
+    case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1>), grid, dim3(256), lds, s, a); return 0;
+    case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2>), grid, dim3(256), lds, s, a); return 0;
+    case 3: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 3>), grid, dim3(256), lds, s, a); return 0;
+    default: return 1;
+  }
+}
+
+template <int D, int RB>
+int launch_partial(const DecodeArgs &a, hipStream_t s) {
+  switch (a.k.bq) {
+    case 1: return launch_partial_bv<D, RB, 1>(a.v.bq, a, s);
+    case 2: return launch_partial_bv<D, RB, 2>(a.v.bq, a, s);
+    case 3: return launch_partial_bv<D, RB, 3>(a.v.bq, a, s);
+    default: return 1;
+  }
+}
+
+template <int D>
+int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
+  const unsigned nq = static_cast<unsigned>(a.batch * a.Hq);
+  hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq), dim3(256), 0, s, a);
+  int e = rb == 1 ? launch_partial<D, 1>(a, s) : launch_partial<D, 2>(a, s);
+  if (e) return e;
+  hipLaunchKernelGGL(decode_merge_fast<D>, dim3(nq), dim3(256), 0, s, a);
+  return 0;
+}
+
+}  // namespace
+
+int launch_decode_fast(int d, int rb, const DecodeArgs &a, hipStream_t s) {
+  int e = 1;
+  if (d == 128) e = launch_fast_d<128>(rb, a, s);
+  else if (d == 256) e = launch_fast_d<256>(rb, a, s);
+  if (e) return e;
+  return hipGetLastError() != hipSuccess;
+}
+
+}  // namespace tq

@@ -107,21 +107,32 @@ namespace tq {
 
 DecodePlan decode_plan(const tq_config &cfg, int32_t batch, int32_t max_len) {
   DecodePlan p{};
+  const int G = cfg.n_kv_heads > 0 ? cfg.n_q_heads / cfg.n_kv_heads : 1;
+  p.fast = (cfg.d == 128 || cfg.d == 256) && (G == 4 || G == 8);
+  p.rb = G >= 4 ? G / 4 : 1;
+  // Split length: a multiple of 256 slots (4 waves x 64), sized for about 2048
+  // work-groups, and capped so that the split's scores (split x G floats) stay
+  // within 32 KB of LDS.
   const int64_t pairs = int64_t(batch) * cfg.n_kv_heads;
-  const int64_t want_wg = 2048;
-  int64_t ns = pairs > 0 ? (want_wg + pairs - 1) / pairs : 1;
-  if (ns < 1) ns = 1;
-  int64_t st = max_len > 0 ? (int64_t(max_len) + ns - 1) / ns : 64;
+  int64_t st = pairs > 0 ? (int64_t(max_len) * pairs + 2047) / 2048 : 256;
+  st = (st + 255) / 256 * 256;
+  const int64_t cap = (8192 / (G > 0 ? G : 1)) / 256 * 256;
+  if (st > cap) st = cap;
   if (st < 256) st = 256;
-  st = (st + 63) / 64 * 64;
   p.split_tokens = static_cast<int32_t>(st);
-  p.n_split = max_len > 0 ? static_cast<int32_t>((int64_t(max_len) + st - 1) / st) : 1;
+  // Splits are aligned to absolute 64-slot tiles, so a sequence may start up to 63
+  // slots into its first split.
+  p.n_split = static_cast<int32_t>((int64_t(max_len) + 63 + st - 1) / st);
+  if (p.n_split < 1) p.n_split = 1;
   p.part_stride = 2 + cfg.d + cfg.m;
   const size_t nq = size_t(batch) * cfg.n_q_heads;
+  const size_t nkv = size_t(batch) * cfg.n_kv_heads;
   size_t o = 0;
-  p.off_qr = o;   o = align256(o + nq * cfg.d * 4);
-  p.off_qs = o;   o = align256(o + nq * cfg.m * 4);
-  p.off_part = o; o = align256(o + nq * size_t(p.n_split) * p.part_stride * 4);
+  p.off_qr = o;     o = align256(o + nq * cfg.d * 4);
+  p.off_qs = o;     o = align256(o + nq * cfg.m * 4);
+  p.off_part = o;   o = align256(o + nq * size_t(p.n_split) * p.part_stride * 4);
+  p.off_qop = o;    o = align256(o + nkv * size_t(p.rb) * 5 * (cfg.d / 64) * 64 * 16);
+  p.off_qconst = o; o = align256(o + nq * 4 * 8);
   p.total = o;
   return p;
 }
@@ -364,9 +375,20 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
   a.part = reinterpret_cast<float *>(ws + p.off_part);
   a.split_tokens = p.split_tokens;
   a.n_split = p.n_split;
+  a.qop = ws + p.off_qop;
+  a.qconst = reinterpret_cast<double *>(ws + p.off_qconst);
+  for (int t = 0; t < 2; ++t) {
+    const tq_codebook &cb = t ? cfg->v.cb : cfg->k.cb;
+    double *wc = t ? a.walsh_v : a.walsh_k;
+    wc[0] = cb.walsh[1];
+    wc[1] = cb.levels > 2 ? cb.walsh[2] : 0.0;
+    wc[2] = cb.levels > 4 ? cb.walsh[4] : 0.0;
+    wc[3] = cb.levels > 4 ? cb.walsh[7] : 0.0;
+  }
   a.out = out;
   a.status = status;
-  if (tq::launch_decode(cfg->d, a, stream) != 0) return TQ_ERR_LAUNCH;
+  const int rc = p.fast ? tq::launch_decode_fast(cfg->d, p.rb, a, stream) : tq::launch_decode(cfg->d, a, stream);
+  if (rc != 0) return TQ_ERR_LAUNCH;
   return TQ_OK;
 }
 

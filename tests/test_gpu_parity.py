@@ -314,3 +314,15 @@ def test_full_workload4_ragged_sampled():
     rng = np.random.default_rng(4)
     pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, w.batch, 3), rng.integers(0, w.n_kv_heads, 3))]
     check_decode(run, out, pairs=pairs, lens=lens1, label="w4-full")
+
+
+@pytest.mark.parametrize("d,hkv,hq", [(128, 2, 4), (64, 1, 16)])
+def test_reference_decode_path(d, hkv, hq):
+    """Shapes outside the matrix-core decode (G = 2; d = 64 with G = 16) run the reference kernels."""
+    w = W.small(W.WORKLOADS[2], d=d, n_kv_heads=hkv, n_q_heads=hq, batch=2, seq_len=300)
+    run = Run(w)
+    _log(f"reference decode path d={d} G={hq // hkv}")
+    dbg = run.quantize()
+    check_quantize(run, dbg, label=f"ref-d{d}")
+    check_decode(run, run.decode(), label=f"ref-d{d}-G{hq // hkv}")
+    assert run.status() == 0
