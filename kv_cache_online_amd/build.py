@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libtq.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-SOURCES = ["tq_host.cpp", "tq_plain.hip", "tq_decode_fast.hip"]
+SOURCES = ["tq_host.cpp", "tq_plain.hip", "tq_decode_fast.hip", "tq_quantize_fast.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -79,6 +79,8 @@ struct QuantArgs {
   const int64_t *dst;
   const float *rotT;
   const float *stT;
+  const uint16_t *rot_hml;  // Pi as three bf16 pieces [3][d][d]
+  const uint16_t *st_hml;   // S~ as three bf16 pieces [3][m][d]
   uint32_t *status;
 };
 
@@ -119,6 +121,7 @@ struct DecodeArgs {
 
 // Host launchers (defined in the .hip translation units).  Return hipError_t.
 int launch_quantize(int d, const QuantArgs &a, hipStream_t s);
+int launch_quantize_fast(int d, const QuantArgs &a, hipStream_t s);
 int launch_decode(int d, const DecodeArgs &a, hipStream_t s);
 int launch_decode_fast(int d, int rb, const DecodeArgs &a, hipStream_t s);
 

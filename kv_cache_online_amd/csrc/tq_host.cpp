@@ -101,6 +101,17 @@ tq::CodebookF32 cb_f32(const tq_codebook &cb) {
   return o;
 }
 
+// The matrix-core quantize decides cells from |u| and the upper half of the
+// codebook, which needs c[L-1-i] == -c[i] and t[L-2-i] == -t[i] in fp32.
+bool cb_symmetric(const tq::CodebookF32 &c) {
+  const int L = c.levels;
+  for (int i = 0; i < L; ++i)
+    if (c.cen[L - 1 - i] != -c.cen[i]) return false;
+  for (int i = 0; i + 1 < L; ++i)
+    if (c.thr[L - 2 - i] != -c.thr[i]) return false;
+  return true;
+}
+
 }  // namespace
 
 namespace tq {
@@ -307,8 +318,12 @@ int tq_quantize_kv(const tq_config *cfg, const void *k, const void *v, tq_dtype 
     a.dst = dst_token;
     a.rotT = reinterpret_cast<const float *>(prep + L.rotT);
     a.stT = reinterpret_cast<const float *>(prep + L.stT);
+    a.rot_hml = reinterpret_cast<const uint16_t *>(prep + L.rot_hml);
+    a.st_hml = reinterpret_cast<const uint16_t *>(prep + L.st_hml);
     a.status = status;
-    if (tq::launch_quantize(cfg->d, a, stream) != 0) return TQ_ERR_LAUNCH;
+    const bool fast = cfg->d == 128 && cb_symmetric(a.t.cb);
+    const int rc = fast ? tq::launch_quantize_fast(cfg->d, a, stream) : tq::launch_quantize(cfg->d, a, stream);
+    if (rc != 0) return TQ_ERR_LAUNCH;
   }
   return TQ_OK;
 }

@@ -1,0 +1,560 @@
+// Matrix-core quantize for d = m = 128 on gfx950.
+//
+// Method: ast-softpro.ru, "Технология TurboQuant и её применение с локальными
+// LLM", section 1.2 "Как работает TurboQuant" -- stage 1 rotates x by Pi and
+// picks a Lloyd-Max cell per coordinate of u = Pi x / ||x||; stage 2 keeps
+// sign(S r) and ||r||_2 of the residual r = x - ||x||~ Pi^T c[idx].  As in the
+// reference-grade kernel, the residual is formed in the rotated frame,
+// rho = Pi x - ||x||~ c[idx], and sketched as S~ rho with S~ = S Pi^T.
+//
+// Both contractions are dense (a 128 x 128 matrix against a tile of vectors),
+// so they run on v_mfma_f32_16x16x32_bf16.  Every operand is split into bf16
+// pieces (hi + mid + lo reproduces an fp32 value exactly); the piece products
+// are exact in fp32, and the dropped cross terms are below 2^-24 relative for
+// Pi x and below 2^-16 relative for the sketch, whose only use is a sign.
+//
+// Work-group: 4 waves, two work-groups per CU so that one group's matrix
+// phase overlaps the other's vector phase; persistent over tiles of 32
+// vectors of one (sequence, head).  Tiles are aligned to 32-slot blocks of the
+// cache.  Wave w owns rotated coordinates and sketch rows 32w .. 32w+31 and
+// keeps those rows of Pi and S~ in registers as the MFMA row operand; the
+// tile of vectors is the column operand, so a lane of the result holds four
+// consecutive coordinates of one vector.  Per tile:
+//   A  load (the next tile is prefetched into registers), ||x||, per-vector
+//      boundaries ||x|| t_k and scaled centroids ||x||~ c_k, input -> LDS
+//   B  z = Pi x; cells by comparing |z| with ||x|| t_k; the compare masks are
+//      the bit planes, one 32-bit word per coordinate over the 32 slots; the
+//      residual's bf16 pieces -> LDS; partial ||rho||^2 per wave
+//   D  p = S~ rho; sign masks the same way; ||rho|| per vector
+//   E  records to HBM: the words are the value layout as they stand; the
+//      token-major key layout takes a 32 x 32 bit transpose per word block
+// The codebook must be symmetric (c[L-1-i] = -c[i], middle boundary 0), as
+// the Lloyd-Max codebook of the symmetric coordinate law is.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "tq_common.h"
+#include "tq_device.h"
+
+namespace tq {
+namespace {
+
+constexpr int QD = 128;      // d = m
+constexpr int QT = 32;       // vectors per tile
+constexpr int QW = 4;        // waves per work-group
+constexpr int QN = 64 * QW;  // threads per work-group
+constexpr int XS = QD + 8;   // bf16 row stride of the operand tiles (elements)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int NPX, int BQ>
+struct QSmem {
+  __align__(16) uint16_t xs[NPX][QT][XS];    // input pieces (bf16 bits)
+  __align__(16) uint16_t rh[QT][XS];         // residual, hi piece
+  __align__(16) uint16_t rm[QT][XS];         // residual, mid piece
+  __align__(16) float vth[QT][8];            // per vector: ||x|| t_k at 0..2, ||x||~ c_k at 4..7
+  __align__(16) float rr[QW][QT];            // ||rho||^2 over each wave's coordinates
+  __align__(16) uint16_t wst[BQ + 1][QD][2]; // words (plane, coordinate), bit = row; plane BQ: signs
+  __align__(16) uint32_t nub[QT];            // fp16 bits of ||x||
+  __align__(16) uint32_t scl[QT];            // nu bits | rho bits << 16
+};
+
+struct Tile {
+  int b, h;
+  int t0;         // token of row 0 (negative when the tile starts before the first token)
+  int64_t base;   // slot of row 0, a multiple of 32
+};
+
+// Division by a run-time constant d >= 1 for dividends below 2^31:
+// q = (umulhi(n, m) + n) >> s with s = ceil(log2 d), m = 2^32 (2^s - d) / d + 1.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+__host__ inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
+  return FastDiv{d, static_cast<uint32_t>(m), s};
+}
+
+__device__ inline uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.s; }
+
+__device__ inline Tile tile_at(const QuantArgs &a, uint32_t tile, FastDiv ftpb, FastDiv fh) {
+  Tile T;
+  const uint32_t bh = fdiv(tile, ftpb);
+  const int k = static_cast<int>(tile - bh * ftpb.d);
+  T.b = static_cast<int>(fdiv(bh, fh));
+  T.h = static_cast<int>(bh - uint32_t(T.b) * fh.d);
+  const int64_t d0 = a.dst[T.b];
+  const int sh = static_cast<int>(d0 & 31);
+  T.base = (d0 - sh) + 32 * int64_t(k);
+  T.t0 = 32 * k - sh;
+  return T;
+}
+
+// Row v, coordinates 16 c16 .. 16 c16 + 15 of a tile (zeros outside the tokens).
+template <bool F32>
+__device__ inline void load_rows(const QuantArgs &a, const Tile &T, int v, int c16, uint4 *r) {
+  constexpr int NV = F32 ? 4 : 2;
+  const int tok = T.t0 + v;
+  if (tok >= 0 && tok < a.n_new) {
+    const size_t row = (size_t(T.b) * a.H + T.h) * size_t(a.n_new) + tok;
+    const uint4 *p = F32 ? reinterpret_cast<const uint4 *>(static_cast<const float *>(a.t.x) + row * QD + 16 * c16)
+                         : reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.t.x) + row * QD + 16 * c16);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) r[i] = p[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) r[i] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// IEEE binary16 bits of v >= 0 by the hardware conversion (round to nearest
+// even); v > 65504 saturates to 65504 and sets *over.  Rounding a float64
+// value through float32 first can differ from a direct rounding only within
+// 2^-24 relative of an fp16 rounding midpoint.
+__device__ inline uint32_t f16_bits_f32(float v, bool *over) {
+  if (!(v == v)) return 0x7E00u;
+  if (v > 65504.0f) {
+    *over = true;
+    return 0x7BFFu;
+  }
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+
+__device__ inline uint32_t cvt_pk_bf16(float a, float b) {
+  const f32x2 p = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+}
+
+// v_writelane_b32 through the compiler's own intrinsic (this clang has no
+// builtin for it), so that its hazard handling sees the instruction: a
+// writelane that reads a compare mask needs wait states after the v_cmp.
+extern "C" __device__ int tq_writelane_i32(int v, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// Lane `lane` of `old` takes the wave-uniform value v (EXEC is ignored).
+__device__ inline uint32_t wlane(uint32_t v, int lane, uint32_t old) {
+  return static_cast<uint32_t>(tq_writelane_i32(static_cast<int>(v), lane, static_cast<int>(old)));
+}
+
+// Transpose a 32 x 32 bit matrix held one row per lane (lanes 0-31 and 32-63
+// each hold one matrix): afterwards bit c of lane l is bit l of row c.
+__device__ inline uint32_t transpose32(uint32_t a, int row) {
+  const uint32_t lo_mask[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int s = 16 >> i;
+    const uint32_t m = lo_mask[i];
+    const uint32_t p = static_cast<uint32_t>(__shfl_xor(static_cast<int>(a), s, kWave));
+    a = (row & s) ? ((a & ~m) | ((p >> s) & m)) : ((a & m) | ((p << s) & ~m));
+  }
+  return a;
+}
+
+// The 16 compare masks of one plane (2 row blocks x 2 column groups x 4
+// registers), gathered into lanes 0..31 of a VGPR and stored as half-words of
+// the (plane, coordinate) words: lane (rb 16 + r 4 + g2 2 + hh) holds mask
+// dword hh, whose low half is coordinate 16 rb + 8 hh + r (vectors 16 g2 ..
+// 16 g2 + 15) and whose high half is that coordinate + 4.
+struct PlaneBits {
+  uint32_t pk = 0;
+  __device__ inline void put(uint64_t m, int rb, int g2, int r) {
+    const int l = rb * 16 + r * 4 + g2 * 2;
+    pk = wlane(static_cast<uint32_t>(m), l, pk);
+    pk = wlane(static_cast<uint32_t>(m >> 32), l + 1, pk);
+  }
+  __device__ inline void store(uint16_t (*w)[2], int lane, int c0) const {
+    if (lane < 32) {
+      const int rb = lane >> 4, r = (lane >> 2) & 3, g2 = (lane >> 1) & 1, hh = lane & 1;
+      const int c = c0 + 16 * rb + 8 * hh + r;
+      w[c][g2] = static_cast<uint16_t>(pk);
+      w[c + 4][g2] = static_cast<uint16_t>(pk >> 16);
+    }
+  }
+};
+
+template <int BQ, bool F32>
+__global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_tiles, FastDiv ftpb, FastDiv fh) {
+  constexpr int NPX = F32 ? 3 : 1;
+  constexpr int NV = F32 ? 4 : 2;
+  constexpr int L = 1 << BQ;
+  constexpr int K = L / 2 - 1;  // positive boundaries
+  __shared__ QSmem<NPX, BQ> sm;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, li = lane & 15, lg = lane >> 4;
+  const int v = t >> 3, c16 = t & 7;  // phase A: row v, coordinates 16 c16 .. 16 c16 + 15
+  const int cw = 32 * w;              // first coordinate / sketch row of this wave
+  const bool sk = a.t.sketch != 0;
+
+  // Row operands: rows cw + 16 rb + li of Pi and S~, 8 consecutive columns per lane group.
+  bf16x8 pia[3][2][4], sta[2][2][4];
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        pia[p][rb][kc] = *reinterpret_cast<const bf16x8 *>(a.rot_hml + (size_t(p) * QD + cw + 16 * rb + li) * QD +
+                                                            32 * kc + 8 * lg);
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        sta[p][rb][kc] = sk ? *reinterpret_cast<const bf16x8 *>(a.st_hml + (size_t(p) * QD + cw + 16 * rb + li) * QD +
+                                                                 32 * kc + 8 * lg)
+                            : bf16x8{};
+
+  float tpos[K > 0 ? K : 1], cpos[K + 1];
+#pragma unroll
+  for (int k = 0; k < K; ++k) tpos[k] = a.t.cb.thr[L / 2 + k];
+#pragma unroll
+  for (int k = 0; k <= K; ++k) cpos[k] = a.t.cb.cen[L / 2 + k];
+
+  uint32_t flags = 0;
+  uint4 xr[NV];
+  uint32_t tile = blockIdx.x;
+  Tile T{};
+  if (tile < n_tiles) {
+    T = tile_at(a, tile, ftpb, fh);
+    load_rows<F32>(a, T, v, c16, xr);
+  }
+  for (; tile < n_tiles; tile += gridDim.x) {
+    const Tile cur = T;
+    uint4 xc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) xc[i] = xr[i];
+    const uint32_t nxt = tile + gridDim.x;
+    if (nxt < n_tiles) {
+      T = tile_at(a, nxt, ftpb, fh);
+      load_rows<F32>(a, T, v, c16, xr);
+    }
+    if (cur.t0 >= a.n_new) continue;  // no token falls in this tile (uniform)
+
+    // ---------------------------------------------------------------- A --
+    {
+      const uint32_t *u = reinterpret_cast<const uint32_t *>(xc);
+      float ssf = 0.0f;
+      if (F32) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ssf = fmaf(__uint_as_float(u[i]), __uint_as_float(u[i]), ssf);
+        uint32_t pc[3][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x0 = __uint_as_float(u[2 * i]), x1 = __uint_as_float(u[2 * i + 1]);
+          const uint32_t h = cvt_pk_bf16(x0, x1);
+          const float r0 = x0 - __uint_as_float(h << 16), r1 = x1 - __uint_as_float(h & 0xFFFF0000u);
+          const uint32_t m = cvt_pk_bf16(r0, r1);
+          pc[0][i] = h;
+          pc[1][i] = m;
+          pc[2][i] = cvt_pk_bf16(r0 - __uint_as_float(m << 16), r1 - __uint_as_float(m & 0xFFFF0000u));
+        }
+#pragma unroll
+        for (int p = 0; p < NPX; ++p)
+#pragma unroll
+          for (int hv = 0; hv < 2; ++hv)
+            *reinterpret_cast<uint4 *>(&sm.xs[p][v][16 * c16 + 8 * hv]) =
+                make_uint4(pc[p][4 * hv], pc[p][4 * hv + 1], pc[p][4 * hv + 2], pc[p][4 * hv + 3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bf16x2 b2 = __builtin_bit_cast(bf16x2, u[i]);
+          ssf = __builtin_amdgcn_fdot2_f32_bf16(b2, b2, ssf, false);
+        }
+        *reinterpret_cast<uint4 *>(&sm.xs[0][v][16 * c16]) = xc[0];
+        *reinterpret_cast<uint4 *>(&sm.xs[0][v][16 * c16 + 8]) = xc[1];
+      }
+#pragma unroll
+      for (int o = 4; o > 0; o >>= 1) ssf += __shfl_xor(ssf, o, kWave);
+      float nu;
+      bool nonfinite = false;
+      if (__builtin_expect(!isfinite(ssf), 0)) {
+        // rare: an element is not finite, or a float32 square overflowed
+        double sd = 0.0;
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float xi = F32 ? __uint_as_float(u[i])
+                               : __uint_as_float((i & 1) ? (u[i >> 1] & 0xFFFF0000u) : (u[i >> 1] << 16));
+          bad |= !isfinite(xi);
+          sd = fma(double(xi), double(xi), sd);
+        }
+#pragma unroll
+        for (int o = 4; o > 0; o >>= 1) {
+          sd += __shfl_xor(sd, o, kWave);
+          bad |= __shfl_xor(static_cast<int>(bad), o, kWave) != 0;
+        }
+        nonfinite = bad;
+        nu = static_cast<float>(sqrt(sd));
+      } else {
+        nu = __builtin_amdgcn_sqrtf(ssf);
+      }
+      if (c16 == 0) {
+        bool over = false;
+        const uint32_t nb = f16_bits_f32(nu, &over);
+        const float n16 = f16_val(nb);
+        f32x4 th = {INFINITY, INFINITY, INFINITY, INFINITY}, cs = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < K; ++k) th[k] = nu > 0.0f ? nu * tpos[k] : INFINITY;
+#pragma unroll
+        for (int k = 0; k <= K; ++k) cs[k] = n16 * cpos[k];
+        *reinterpret_cast<f32x4 *>(&sm.vth[v][0]) = th;
+        *reinterpret_cast<f32x4 *>(&sm.vth[v][4]) = cs;
+        sm.nub[v] = nb;
+        const int tok = cur.t0 + v;
+        if (tok >= 0 && tok < a.n_new) {
+          if (nonfinite) flags |= TQ_FLAG_NONFINITE_INPUT;
+          if (over) flags |= TQ_FLAG_SCALE_OVERFLOW;
+          if (a.t.dbg) a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2] = nu;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- B --
+    {
+      f32x4 acc[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) acc[rb][g2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        bf16x8 xb[2][NPX];
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+          for (int px = 0; px < NPX; ++px)
+            xb[g2][px] = *reinterpret_cast<const bf16x8 *>(&sm.xs[px][16 * g2 + li][32 * kc + 8 * lg]);
+#pragma unroll
+        for (int px = 0; px < NPX; ++px)
+#pragma unroll
+          for (int pp = 0; pp < (F32 ? 3 - px : 3); ++pp)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int g2 = 0; g2 < 2; ++g2)
+                acc[rb][g2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pia[pp][rb][kc], xb[g2][px], acc[rb][g2], 0, 0, 0);
+      }
+      // acc[rb][g2] lane (li, lg) register r: coordinate cw + 16 rb + 4 lg + r of vector 16 g2 + li
+      PlaneBits pb[BQ];
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int vv = 16 * g2 + li;
+        const f32x4 th = *reinterpret_cast<const f32x4 *>(&sm.vth[vv][0]);
+        const f32x4 cs = *reinterpret_cast<const f32x4 *>(&sm.vth[vv][4]);
+        float rr = 0.0f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float rho[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float z = acc[rb][g2][r];
+            const float az = fabsf(z);
+            const bool pos = z >= 0.0f;
+            float val = cs[0];
+            uint64_t cm[K > 0 ? K : 1];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+              const bool c = az >= th[k];
+              val = c ? cs[k + 1] : val;
+              cm[k] = __ballot(c);
+            }
+            rho[r] = z - (pos ? val : -val);
+            rr = fmaf(rho[r], rho[r], rr);
+            const uint64_t pm = __ballot(pos);
+            // cell = L/2 + m above zero, L/2 - 1 - m below, with m the number of
+            // positive boundaries <= |u|; bit q < BQ-1 of m is the parity of the
+            // compares at multiples of 2^q (the compares form a thermometer code).
+#pragma unroll
+            for (int q = 0; q < BQ; ++q) {
+              uint64_t bits = pm;
+              if (q < BQ - 1) {
+                uint64_t mq = 0;
+#pragma unroll
+                for (int k = 1; k <= K; ++k)
+                  if ((k & ((1 << q) - 1)) == 0) mq ^= cm[k - 1];
+                bits = ~(mq ^ pm);
+              }
+              pb[q].put(bits, rb, g2, r);
+            }
+          }
+          if (sk) {
+            const uint32_t h01 = cvt_pk_bf16(rho[0], rho[1]), h23 = cvt_pk_bf16(rho[2], rho[3]);
+            const uint32_t m01 =
+                cvt_pk_bf16(rho[0] - __uint_as_float(h01 << 16), rho[1] - __uint_as_float(h01 & 0xFFFF0000u));
+            const uint32_t m23 =
+                cvt_pk_bf16(rho[2] - __uint_as_float(h23 << 16), rho[3] - __uint_as_float(h23 & 0xFFFF0000u));
+            const int c = cw + 16 * rb + 4 * lg;
+            *reinterpret_cast<uint2 *>(&sm.rh[vv][c]) = make_uint2(h01, h23);
+            *reinterpret_cast<uint2 *>(&sm.rm[vv][c]) = make_uint2(m01, m23);
+          }
+        }
+        if (sk) {
+          rr += __shfl_xor(rr, 16, kWave);
+          rr += __shfl_xor(rr, 32, kWave);
+          if (lg == 0) sm.rr[w][vv] = rr;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < BQ; ++q) pb[q].store(sm.wst[q], lane, cw);
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- D --
+    {
+      uint32_t rbits = 0;
+      if (sk) {
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) acc[rb][g2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          bf16x8 bh[2], bm[2];
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            bh[g2] = *reinterpret_cast<const bf16x8 *>(&sm.rh[16 * g2 + li][32 * kc + 8 * lg]);
+            bm[g2] = *reinterpret_cast<const bf16x8 *>(&sm.rm[16 * g2 + li][32 * kc + 8 * lg]);
+          }
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int g2 = 0; g2 < 2; ++g2)
+              acc[rb][g2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sta[0][rb][kc], bh[g2], acc[rb][g2], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int g2 = 0; g2 < 2; ++g2)
+              acc[rb][g2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sta[1][rb][kc], bh[g2], acc[rb][g2], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int g2 = 0; g2 < 2; ++g2)
+              acc[rb][g2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sta[0][rb][kc], bm[g2], acc[rb][g2], 0, 0, 0);
+        }
+        PlaneBits ps;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ps.put(__ballot(acc[rb][g2][r] >= 0.0f), rb, g2, r);
+        ps.store(sm.wst[BQ], lane, cw);
+        if (t < QT) {
+          float rr = 0.0f;
+#pragma unroll
+          for (int ww = 0; ww < QW; ++ww) rr += sm.rr[ww][t];
+          const float rho = __builtin_amdgcn_sqrtf(rr);
+          bool over = false;
+          rbits = f16_bits_f32(rho, &over);
+          const int tok = cur.t0 + t;
+          if (tok >= 0 && tok < a.n_new) {
+            if (over) flags |= TQ_FLAG_SCALE_OVERFLOW;
+            if (a.t.dbg) a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = rho;
+          }
+        }
+      } else if (t < QT) {
+        const int tok = cur.t0 + t;
+        if (tok >= 0 && tok < a.n_new && a.t.dbg)
+          a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = 0.0f;
+      }
+      if (t < QT) sm.scl[t] = sm.nub[t] | (rbits << 16);
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- E --
+    {
+      const bool in_range = cur.base >= 0 && cur.base < a.t.cap;  // base and cap are multiples of 32
+      const int lo = cur.t0 < 0 ? -cur.t0 : 0;
+      const int hi = a.n_new - cur.t0 < QT ? a.n_new - cur.t0 : QT;
+      const uint32_t vm = hi - lo >= 32 ? 0xFFFFFFFFu : (((1u << (hi - lo)) - 1u) << lo);
+      const int npl = BQ + (sk ? 1 : 0);
+      if (!in_range) {
+        flags |= TQ_FLAG_OUT_OF_RANGE;
+      } else {
+        const int64_t hs0 = int64_t(cur.h) * a.t.cap + cur.base;
+        if (t < QT && ((vm >> t) & 1)) *reinterpret_cast<uint32_t *>(a.t.scl + (hs0 + t) * 2) = sm.scl[t];
+        if (a.t.layout == TQ_LAYOUT_BLOCK32) {
+          // the (plane, coordinate) words are the value layout's words of this block
+          const int64_t b0 = int64_t(cur.h) * (a.t.cap / 32) + (cur.base >> 5);
+          for (int c = t; c < npl * QD; c += QN) {
+            const int pl = c / QD, cc = c % QD;
+            const uint32_t word = *reinterpret_cast<const uint32_t *>(&sm.wst[pl][cc][0]);
+            uint32_t *dw = pl < BQ ? a.t.idx + (b0 * BQ + pl) * QD + cc : a.t.sgn + b0 * QD + cc;
+            if (vm == 0xFFFFFFFFu) {
+              *dw = word;
+            } else {
+              atomicAnd(dw, ~vm);
+              atomicOr(dw, word & vm);
+            }
+          }
+        } else {
+          // token-major: transpose each 32 x 32 block (plane, coordinate word) to per-slot words
+          for (int b2 = 0; b2 < npl * 4; b2 += 2 * QW) {
+            const int blk = b2 + 2 * w + (lane >> 5), row = lane & 31;
+            const int pl = blk >> 2, wd = blk & 3;
+            const bool act = blk < npl * 4;
+            uint32_t word = act ? *reinterpret_cast<const uint32_t *>(&sm.wst[pl][32 * wd + row][0]) : 0u;
+            word = transpose32(word, row);  // lane row now holds slot base + row
+            if (act && ((vm >> row) & 1)) {
+              uint32_t *dw = pl < BQ ? a.t.idx + ((hs0 + row) * BQ + pl) * 4 + wd : a.t.sgn + (hs0 + row) * 4 + wd;
+              *dw = word;
+            }
+          }
+        }
+      }
+    }
+  }
+  if (a.status) {
+    const uint64_t f1 = __ballot(flags & 1u), f2 = __ballot(flags & 2u), f4 = __ballot(flags & 4u);
+    const uint32_t f = (f1 ? 1u : 0u) | (f2 ? 2u : 0u) | (f4 ? 4u : 0u);
+    if (lane == 0 && f) atomicOr(a.status, f);
+  }
+}
+
+template <int BQ, bool F32>
+int launch_q(const QuantArgs &a, hipStream_t s) {
+  const int64_t tpb = (int64_t(a.n_new) + QT - 1) / QT + 1;
+  const int64_t n_tiles = int64_t(a.batch) * a.H * tpb;
+  if (n_tiles >= (int64_t(1) << 31)) return 1;
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, quantize_mfma<BQ, F32>, QN, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const int64_t full = int64_t(per_cu) * cus;
+  const unsigned grid = static_cast<unsigned>(n_tiles < full ? n_tiles : full);
+  if (grid == 0) return 0;
+  hipLaunchKernelGGL((quantize_mfma<BQ, F32>), dim3(grid), dim3(QN), 0, s, a, static_cast<uint32_t>(n_tiles),
+                     make_fastdiv(static_cast<uint32_t>(tpb)), make_fastdiv(static_cast<uint32_t>(a.H)));
+  return hipGetLastError() != hipSuccess;
+}
+
+}  // namespace
+
+int launch_quantize_fast(int d, const QuantArgs &a, hipStream_t s) {
+  if (d != QD) return 1;
+  const bool f32 = a.dtype == TQ_F32;
+  switch (a.t.bq) {
+    case 1: return f32 ? launch_q<1, true>(a, s) : launch_q<1, false>(a, s);
+    case 2: return f32 ? launch_q<2, true>(a, s) : launch_q<2, false>(a, s);
+    case 3: return f32 ? launch_q<3, true>(a, s) : launch_q<3, false>(a, s);
+    default: return 1;
+  }
+}
+
+}  // namespace tq
