@@ -59,7 +59,7 @@ class TQError(RuntimeError):
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"libtq.so is not built ({_LIB_PATH}); run "
-                          "`python -m kv_cache_online_amd.build` (needs hipcc)")
+                          "`python kv_cache_online_amd/build.py` (needs hipcc)")
     lib = ctypes.CDLL(_LIB_PATH)
     lib.tq_build_codebook.argtypes = [c_int32, c_double, POINTER(tq_codebook)]
     lib.tq_build_codebook.restype = c_int

@@ -1,6 +1,8 @@
 """Build libtq.so in-tree with hipcc for gfx950.
 
-    python -m kv_cache_online_amd.build [-v]
+    python kv_cache_online_amd/build.py [-v]
+
+(run as a script: importing the package itself needs the built library)
 
 Every HIP source is compiled with packed-FP32 instruction selection turned off
 (-Xclang -target-feature -Xclang -packed-fp32-ops); the host pass warns that it

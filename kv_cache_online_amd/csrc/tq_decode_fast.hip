@@ -42,7 +42,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kSigPlane = 4;     // operand / accumulator slot of the sign plane
-constexpr int kScoreFloats = 8192;
 
 __device__ inline int n_walsh(int bq) { return bq == 3 ? 4 : bq; }
 
@@ -141,82 +140,82 @@ __device__ inline void clip_seq(const DecodeArgs &a, int b, int64_t *start, int6
 }
 
 // ------------------------------------------------------------- query prep ---
-// One block per (sequence, query head): q_rot = Pi q and q_s = S q in float64,
-// then this head's four rows (one per digit) of every score operand, written
-// as 16-byte lane entries, and the exact correction constants
-// sum_j F_j 2^shift_j.
+// One block per (sequence, query head): q_rot = Pi q and q_s = S q in fp32
+// (one matrix row per thread, the row's loads issued together; the products
+// carry about 2^-24 relative error, far inside what the scores need), then this
+// head's four rows (one per digit) of every score operand, written as 16-byte
+// lane entries, and the exact correction constants sum_j F_j 2^shift_j.
+// Reductions run on wave shuffles, so the block needs four barriers.
 template <int D>
 __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   constexpr int C = D / 64;
-  __shared__ double q[D], qr[D], qs[D];
-  __shared__ double red[2][256];
-  __shared__ double pj[256 / (D / 4)][2][D];
-  const int tid = threadIdx.x;
+  constexpr int RPT = 2 * D / 256;  // matrix rows per thread (rows 0..D-1: Pi, D..2D-1: S)
+  constexpr int CH = 32 / RPT;      // float4 loads in flight per row chunk
+  __shared__ __attribute__((aligned(16))) float q[D];
+  __shared__ float qr[D], qs[D];
+  __shared__ float wmax[2][4];
+  __shared__ double wsum[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.x, b = bh / a.Hq, hq = bh % a.Hq;
   const int kvh = hq / a.G, hl = hq % a.G, rb = hl >> 2, row0 = (hl & 3) * 4;
   const int RB = a.G / 4;
+  // the matrix rows do not depend on q: issue their first chunk before q arrives
+  float4 m0[RPT][CH];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int r = tid + 256 * u;
+    const float4 *row = reinterpret_cast<const float4 *>((r < D ? a.rot : a.proj) + size_t(r < D ? r : r - D) * D);
+#pragma unroll
+    for (int k = 0; k < CH; ++k) m0[u][k] = row[k];
+  }
   for (int j = tid; j < D; j += 256) q[j] = load_q(a.q, a.dtype, size_t(bh) * D + j);
   __syncthreads();
-  // q_rot[j] = sum_k Pi[j][k] q[k] (rows of Pi^T), q_s likewise with S^T:
-  // thread (kg, jg) sums rows k of its k range for 4 consecutive columns
-  {
-    constexpr int JG = D / 4, KG = 256 / JG, KPER = D / KG;
-    const int jg = tid % JG, kg = tid / JG;
-    double xr[4] = {0.0, 0.0, 0.0, 0.0}, xs[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 8
-    for (int kk = 0; kk < KPER; ++kk) {
-      const int k = kg * KPER + kk;
-      const float4 r = *reinterpret_cast<const float4 *>(a.rotT + size_t(k) * D + 4 * jg);
-      const float4 t = *reinterpret_cast<const float4 *>(a.projT + size_t(k) * D + 4 * jg);
-      const double qk = q[k];
-      xr[0] = fma(double(r.x), qk, xr[0]);
-      xr[1] = fma(double(r.y), qk, xr[1]);
-      xr[2] = fma(double(r.z), qk, xr[2]);
-      xr[3] = fma(double(r.w), qk, xr[3]);
-      xs[0] = fma(double(t.x), qk, xs[0]);
-      xs[1] = fma(double(t.y), qk, xs[1]);
-      xs[2] = fma(double(t.z), qk, xs[2]);
-      xs[3] = fma(double(t.w), qk, xs[3]);
-    }
+  float mr = 0.0f, ms = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      pj[kg][0][4 * jg + u] = xr[u];
-      pj[kg][1][4 * jg + u] = xs[u];
+  for (int u = 0; u < RPT; ++u) {
+    const int r = tid + 256 * u;
+    const bool isr = r < D;
+    const float4 *row = reinterpret_cast<const float4 *>((isr ? a.rot : a.proj) + size_t(isr ? r : r - D) * D);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k0 = 0; k0 < D / 4; k0 += CH) {
+      float4 m[CH];
+#pragma unroll
+      for (int k = 0; k < CH; ++k) m[k] = k0 == 0 ? m0[u][k] : row[k0 + k];
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        const float4 x = *reinterpret_cast<const float4 *>(&q[4 * (k0 + k)]);
+        acc[0] = fmaf(m[k].x, x.x, acc[0]);
+        acc[1] = fmaf(m[k].y, x.y, acc[1]);
+        acc[2] = fmaf(m[k].z, x.z, acc[2]);
+        acc[3] = fmaf(m[k].w, x.w, acc[3]);
+      }
+    }
+    const float v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if (isr) {
+      qr[r] = v;
+      mr = fmaxf(mr, fabsf(v));
+    } else {
+      qs[r - D] = v;
+      ms = fmaxf(ms, fabsf(v));
     }
   }
-  __syncthreads();
-  for (int j = tid; j < D; j += 256) {
-    constexpr int KG = 256 / (D / 4);
-    double vr = 0.0, vs = 0.0;
 #pragma unroll
-    for (int g = 0; g < KG; ++g) {
-      vr += pj[g][0][j];
-      vs += pj[g][1][j];
-    }
-    qr[j] = vr;
-    qs[j] = vs;
+  for (int o = 32; o > 0; o >>= 1) {
+    mr = fmaxf(mr, __shfl_xor(mr, o, kWave));
+    ms = fmaxf(ms, __shfl_xor(ms, o, kWave));
+  }
+  if (lane == 0) {
+    wmax[0][wave] = mr;
+    wmax[1][wave] = ms;
   }
   __syncthreads();
   const int npk = n_walsh(a.k.bq);
   double amax = 0.0;
   for (int p = 0; p < npk; ++p) amax = fmax(amax, fabs(a.walsh_k[p]));
-  double mr = 0.0, ms = 0.0;
-  for (int j = tid; j < D; j += 256) {
-    mr = fmax(mr, fabs(qr[j]));
-    ms = fmax(ms, fabs(qs[j]));
-  }
-  red[0][tid] = mr;
-  red[1][tid] = ms;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) {
-      red[0][tid] = fmax(red[0][tid], red[0][tid + o]);
-      red[1][tid] = fmax(red[1][tid], red[1][tid + o]);
-    }
-    __syncthreads();
-  }
-  const int Ei = fix_exp(amax * red[0][0]), Es = fix_exp(red[1][0]);
-  __syncthreads();
+  const float maxr = fmaxf(fmaxf(wmax[0][0], wmax[0][1]), fmaxf(wmax[0][2], wmax[0][3]));
+  const float maxs = fmaxf(fmaxf(wmax[1][0], wmax[1][1]), fmaxf(wmax[1][2], wmax[1][3]));
+  const int Ei = fix_exp(amax * maxr), Es = fix_exp(maxs);
   uint4 *op = reinterpret_cast<uint4 *>(static_cast<unsigned char *>(a.qop) +
                                         (size_t(b * a.Hkv + kvh) * RB + rb) * 5 * C * kWave * 16);
   const int nplane = npk + a.k.sketch;
@@ -225,41 +224,42 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   for (int e = tid; e < nplane * C * 16; e += 256) {
     const int l = e & 3, g = (e >> 2) & 3, c = (e >> 4) % C, pidx = (e >> 4) / C;
     const bool sign = pidx == npk;
+    const float wk = sign ? 1.0f : static_cast<float>(a.walsh_k[pidx]);
+    const int E = sign ? Es : Ei;
     uint32_t wv[4] = {0u, 0u, 0u, 0u};
-    double ksum = 0.0;
+    int64_t ksum = 0;
 #pragma unroll
     for (int sv = 0; sv < 4; ++sv)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int par = g & 1;
-        const int j = 32 * ((g >> 1) * C + c) + 8 * i + sv + 4 * par;
-        const double v = sign ? qs[j] : a.walsh_k[pidx] * qr[j];
-        const double F = rint(ldexp(v, (sign ? Es : Ei) - sv));
-        ksum += ldexp(F, sv);
-        const uint32_t dg = digits(static_cast<int32_t>(F));
+        const int j = 32 * ((g >> 1) * C + c) + 8 * i + sv + 4 * (g & 1);
+        const float v = sign ? qs[j] : wk * qr[j];
+        const int32_t F = static_cast<int32_t>(rintf(ldexpf(v, E - sv)));
+        ksum += int64_t(F) * (int64_t(1) << sv);
+        const uint32_t dg = digits(F);
         wv[sv] |= ((dg >> (8 * l)) & 0xFFu) << (8 * i);
       }
     if (l == 0) {
-      if (sign) ks += ksum;
-      else ki += ksum;
+      if (sign) ks += double(ksum);
+      else ki += double(ksum);
     }
     const int slot = sign ? kSigPlane : pidx;
     op[(size_t(slot) * C + c) * kWave + 16 * g + row0 + l] = uint4{wv[0], wv[1], wv[2], wv[3]};
   }
-  red[0][tid] = ki;
-  red[1][tid] = ks;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) {
-      red[0][tid] += red[0][tid + o];
-      red[1][tid] += red[1][tid + o];
-    }
-    __syncthreads();
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ki += __shfl_xor(ki, o, kWave);
+    ks += __shfl_xor(ks, o, kWave);
   }
+  if (lane == 0) {
+    wsum[0][wave] = ki;
+    wsum[1][wave] = ks;
+  }
+  __syncthreads();
   if (tid == 0) {
     const double base = double(a.sm_scale) * 1.4426950408889634;  // log2(e): scores in base 2
-    a.qconst[size_t(bh) * 4 + 0] = red[0][0];
-    a.qconst[size_t(bh) * 4 + 1] = red[1][0];
+    a.qconst[size_t(bh) * 4 + 0] = (wsum[0][0] + wsum[0][1]) + (wsum[0][2] + wsum[0][3]);
+    a.qconst[size_t(bh) * 4 + 1] = (wsum[1][0] + wsum[1][1]) + (wsum[1][2] + wsum[1][3]);
     a.qconst[size_t(bh) * 4 + 2] = ldexp(base, -Ei);
     a.qconst[size_t(bh) * 4 + 3] = ldexp(base * double(a.kappa), -Es);
   }
@@ -590,89 +590,118 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
 // ----------------------------------------------------------------- merge ---
 // One block per (sequence, query head): log-sum-exp merge of the split
 // partials, then out = (Pi^T A + kappa S^T B) / l.
-// Thread (sg, eg), sg = tid / 16, eg = tid % 16, sums splits sg, sg + 16, ...
-// for the EPT consecutive elements eg * EPT of (A, B) with vector loads, so
-// many loads are in flight; the 16 split groups are then reduced in LDS.  A
-// split with no tokens has weight 0 and unwritten A, B, which are masked.
-// The projection tiles k across 256 / (D / 4) thread groups (float4 columns).
+// Thread (sg, eg), sg = tid / 16, eg = tid % 16, merges splits sg, sg + 16, ...
+// for the EPT consecutive elements eg * EPT of (A, B) with a running maximum,
+// loading NBT splits at a time before using any of them; the 16 split groups
+// are then combined in LDS.  A split with no tokens (l = 0) has unwritten A, B
+// and is skipped.  The projection tiles k across 256 / (D / 4) thread groups.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_fast(DecodeArgs a) {
-  constexpr int EPT = 2 * D / 16;                 // elements of (A, B) per thread
-  constexpr int JG = D / 4, KG = 256 / JG, KPER = D / KG;
-  __shared__ float red[256];
+  constexpr int EPT = 2 * D / 16;  // elements of (A, B) per thread
+  constexpr int NBT = D == 128 ? 4 : 2;
+  constexpr int JG = D / 4, KG = 256 / JG, KPER = D / KG, KCH = 16;
   __shared__ __attribute__((aligned(16))) float part_s[16][2 * D];
+  __shared__ float ms_s[16], ls_s[16];
   __shared__ __attribute__((aligned(16))) float AB[2 * D];
   __shared__ __attribute__((aligned(16))) float prj[KG][D];
   const int tid = threadIdx.x, sg = tid >> 4, eg = tid & 15;
   const size_t bh = blockIdx.x;
   const int stride = 2 + 2 * D, ns = a.n_split;
   const float *base = a.part + bh * ns * stride;
-  float M = -INFINITY;
-  for (int s = tid; s < ns; s += 256)
-    if (base[size_t(s) * stride + 1] > 0.0f) M = fmaxf(M, base[size_t(s) * stride]);
-  red[tid] = M;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
+  // the projection rows of the first chunk do not depend on the partials:
+  // issue them first
+  const int jg = tid % JG, kg = tid / JG;
+  const bool skv = a.v.sketch != 0;
+  float4 r0[KCH], sp0[KCH];
+#pragma unroll
+  for (int kk = 0; kk < KCH; ++kk) {
+    const int k = kg * KPER + kk;
+    r0[kk] = *reinterpret_cast<const float4 *>(a.rot + size_t(k) * D + 4 * jg);
+    sp0[kk] = skv ? *reinterpret_cast<const float4 *>(a.proj + size_t(k) * D + 4 * jg) : float4{0, 0, 0, 0};
   }
-  M = red[0];
-  __syncthreads();
+  float m_run = -INFINITY, l_run = 0.0f;
   float acc[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) acc[e] = 0.0f;
-  float lpart = 0.0f;
-  for (int s = sg; s < ns; s += 16) {
-    const float *p = base + size_t(s) * stride;
-    const float l = p[1];
-    const float w = l > 0.0f ? expf(p[0] - M) : 0.0f;
-    if (eg == 0) lpart = fmaf(w, l > 0.0f ? l : 0.0f, lpart);
-    // partial records are 2 + 2D floats: element 2 + e sits 8 bytes past a
-    // 16-byte boundary, so read as float2 pairs
-    const float2 *q = reinterpret_cast<const float2 *>(p + 2 + eg * EPT);
+  for (int s0 = sg; s0 < ns; s0 += 16 * NBT) {
+    float pm[NBT], pl[NBT];
+    float2 x[NBT][EPT / 2];
 #pragma unroll
-    for (int e = 0; e < EPT / 2; ++e) {
-      const float2 x = q[e];
-      acc[2 * e] = fmaf(w, w != 0.0f ? x.x : 0.0f, acc[2 * e]);
-      acc[2 * e + 1] = fmaf(w, w != 0.0f ? x.y : 0.0f, acc[2 * e + 1]);
+    for (int u = 0; u < NBT; ++u) {
+      const int s = s0 + 16 * u;
+      pm[u] = -INFINITY;
+      pl[u] = 0.0f;
+      if (s < ns) {
+        const float *p = base + size_t(s) * stride;
+        pm[u] = p[0];
+        pl[u] = p[1];
+        // records are 2 + 2D floats: element 2 + e sits 8 bytes past a 16-byte
+        // boundary, so read as float2 pairs
+        const float2 *q = reinterpret_cast<const float2 *>(p + 2 + eg * EPT);
+#pragma unroll
+        for (int e = 0; e < EPT / 2; ++e) x[u][e] = q[e];
+      }
     }
+#pragma unroll
+    for (int u = 0; u < NBT; ++u) {
+      if (pl[u] > 0.0f) {
+        const float mn = fmaxf(m_run, pm[u]);
+        const float co = expf(m_run - mn), w = expf(pm[u] - mn);
+        l_run = fmaf(l_run, co, w * pl[u]);
+#pragma unroll
+        for (int e = 0; e < EPT / 2; ++e) {
+          acc[2 * e] = fmaf(acc[2 * e], co, w * x[u][e].x);
+          acc[2 * e + 1] = fmaf(acc[2 * e + 1], co, w * x[u][e].y);
+        }
+        m_run = mn;
+      }
+    }
+  }
+  if (eg == 0) {
+    ms_s[sg] = m_run;
+    ls_s[sg] = l_run;
   }
 #pragma unroll
   for (int e = 0; e < EPT; ++e) part_s[sg][eg * EPT + e] = acc[e];
-  red[tid] = lpart;
   __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < 16; ++g) M = fmaxf(M, ls_s[g] > 0.0f ? ms_s[g] : -INFINITY);
+  float wg[16], l = 0.0f;
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    wg[g] = ls_s[g] > 0.0f ? expf(ms_s[g] - M) : 0.0f;
+    l = fmaf(wg[g], ls_s[g], l);
+  }
   for (int e = tid; e < 2 * D; e += 256) {
     float v = 0.0f;
 #pragma unroll
-    for (int g = 0; g < 16; ++g) v += part_s[g][e];
+    for (int g = 0; g < 16; ++g) v = fmaf(wg[g], part_s[g][e], v);
     AB[e] = v;
   }
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const float l = red[0];
+  __syncthreads();
   // projection: thread (kg, jg) sums rows k in [kg * KPER, (kg + 1) * KPER) for
-  // output columns 4 jg .. 4 jg + 3
+  // output columns 4 jg .. 4 jg + 3, KCH rows' loads at a time
   {
-    const int jg = tid % JG, kg = tid / JG;
     float4 x = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-    for (int kk = 0; kk < KPER; ++kk) {
-      const int k = kg * KPER + kk;
-      const float4 r = *reinterpret_cast<const float4 *>(a.rot + size_t(k) * D + 4 * jg);
-      const float av = AB[k];
-      x.x = fmaf(r.x, av, x.x);
-      x.y = fmaf(r.y, av, x.y);
-      x.z = fmaf(r.z, av, x.z);
-      x.w = fmaf(r.w, av, x.w);
-      if (a.v.sketch) {
-        const float4 sp = *reinterpret_cast<const float4 *>(a.proj + size_t(k) * D + 4 * jg);
-        const float bv = a.kappa * AB[D + k];
-        x.x = fmaf(sp.x, bv, x.x);
-        x.y = fmaf(sp.y, bv, x.y);
-        x.z = fmaf(sp.z, bv, x.z);
-        x.w = fmaf(sp.w, bv, x.w);
+#pragma unroll 1
+    for (int k0 = 0; k0 < KPER; k0 += KCH) {
+      float4 r[KCH], sp[KCH];
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        const int k = kg * KPER + k0 + kk;
+        r[kk] = k0 == 0 ? r0[kk] : *reinterpret_cast<const float4 *>(a.rot + size_t(k) * D + 4 * jg);
+        sp[kk] = k0 == 0 ? sp0[kk]
+                         : (skv ? *reinterpret_cast<const float4 *>(a.proj + size_t(k) * D + 4 * jg) : float4{0, 0, 0, 0});
+      }
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        const int k = kg * KPER + k0 + kk;
+        const float av = AB[k], bv = a.kappa * AB[D + k];
+        x.x = fmaf(sp[kk].x, bv, fmaf(r[kk].x, av, x.x));
+        x.y = fmaf(sp[kk].y, bv, fmaf(r[kk].y, av, x.y));
+        x.z = fmaf(sp[kk].z, bv, fmaf(r[kk].z, av, x.z));
+        x.w = fmaf(sp[kk].w, bv, fmaf(r[kk].w, av, x.w));
       }
     }
     *reinterpret_cast<float4 *>(&prj[kg][4 * jg]) = x;
