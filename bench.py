@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, spec
-FP64_VEC_PEAK_TFLOPS = 78.6    # MI355X vector fp64, spec
+BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix, spec
 METRIC = "packed-KV decode-attention GB/s (% HBM peak); KV quantize tokens/s"
 
 
@@ -46,8 +46,9 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_key):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+def traffic_for(prefixes):
+    """HBM bytes per call (sum over the call's kernels, each by name prefix) from
+    the committed rocprofv3 counter runs, if they were taken on this source."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -57,7 +58,62 @@ def traffic_for(kernel_key):
         return None
     if t.get("source_hash") != source_hash():
         return None
-    return t.get("kernels", {}).get(kernel_key)
+    ks = t.get("kernels", {})
+    total = 0.0
+    for pre, n in prefixes:
+        hit = [v["bytes"] for k, v in ks.items() if k.startswith(pre)]
+        if not hit:
+            return None
+        total += n * hit[0]
+    return total
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """Plain device-to-device copies of a known size, for scaling HBM byte counters."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
+    """profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of
+    this bench and of copy_calibration (counters in KiB per dispatch).  Each
+    counter is scaled by bytes / counter of the plain copy: FETCH against the
+    bytes the copy reads, WRITE against the bytes it writes."""
+    import csv
+    import re
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") != counter:
+                continue
+            k = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].split("::")[-1]
+            vals.setdefault(k, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sorted(v)[len(v) // 2] for k, v in vals.items()}
+
+    cf = per_kernel(copy_fetch_csv, "FETCH_SIZE")
+    cw = per_kernel(copy_write_csv, "WRITE_SIZE")
+    ck = max(cf, key=cf.get)                      # the copy is the largest dispatch
+    f_scale, w_scale = copy_bytes / cf[ck], copy_bytes / cw[ck]
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    kernels = {}
+    for k in fetch:
+        if k in write and k.startswith(("quantize", "decode")):
+            kernels[k] = {"fetch_bytes": fetch[k] * f_scale, "write_bytes": write[k] * w_scale,
+                          "bytes": fetch[k] * f_scale + write[k] * w_scale}
+    out = {"source_hash": source_hash(), "copy_kernel": ck, "copy_bytes": copy_bytes,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(w, rot, proj, seconds):
@@ -84,7 +140,7 @@ def cpu_baseline(w, rot, proj, seconds):
     f16 = lambda b: np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
     reps, t_dec = 0, 0.0
     t_start = time.perf_counter()
-    while reps < 1 or (time.perf_counter() - t_start < seconds / 2 and reps < 20):
+    while reps < 1 or (time.perf_counter() - t_start < seconds / 2 and reps < 40):
         t0 = time.perf_counter()
         i, s, nb, rb = O.unpack_token_major(*kp, w.bits_mse)
         kh = O.dequantize(i, s, f16(nb), f16(rb), rot, proj, cb)
@@ -96,7 +152,7 @@ def cpu_baseline(w, rot, proj, seconds):
     rec = O.record_bytes(w.d, w.m, w.bits_mse, w.sketch)
     dec_gbs = reps * T * 2 * rec / t_dec / 1e9
     # quantize: token positions (K and V of every kv head) on a sample of vectors
-    n_pos = 8192
+    n_pos = 49152
     X = W.to_f64(W.kv_chunk(w, 0, 0, 1, n_tokens=n_pos * w.n_kv_heads * 2), w.dtype)
     t0 = time.perf_counter()
     qq = O.quantize(X, rot, proj, cb)
@@ -118,7 +174,14 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="rotation copies (0: enough for 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only plain 1 GiB device copies (HBM counter calibration)")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 counter CSVs (no GPU)")
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(*args.traffic, copy_bytes=1 << 30)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this hot path runs on one GPU; multi-GPU runs are not part of this build "
@@ -132,6 +195,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        copy_calibration()
+        return
     w = W.WORKLOADS[args.workload]
     rot, proj = W.rotation(w.d, w.wid), W.sketch(w.m, w.d, w.wid)
     s = TQSession(w.d, w.n_kv_heads, w.n_q_heads, rot, proj, k_bits=w.bits_mse, v_bits=w.bits_mse,
@@ -200,27 +266,34 @@ def main():
     q_gbs = q_bytes / q_avg / 1e9
     q_tok = B * T / q_avg
     q_flops = 2 * B * H * T * 4 * d * d           # two d x d contractions per vector
-    roof_dec = {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": dec_gbs / HBM_PEAK_GBS, "traffic": traffic_for("decode"),
-                "kernel": "tq_decode_attention (query prep + split partials + merge)",
-                "bytes_per_launch": packed_bytes, "avg_launch_s": d_avg}
-    roof_q_hbm = {"bound": "hbm", "achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": q_gbs / HBM_PEAK_GBS}
     q_tf = q_flops / q_avg / 1e12
-    roof_q = {"bound": "alu", "achieved": q_tf, "peak": FP64_VEC_PEAK_TFLOPS, "unit": "TFLOP/s",
-              "frac": q_tf / FP64_VEC_PEAK_TFLOPS, "traffic": traffic_for("quantize"),
-              "kernel": "tq_quantize_kv (K and V launches)", "flops_per_launch": q_flops,
-              "bytes_per_launch": q_bytes, "avg_launch_s": q_avg, "hbm": roof_q_hbm}
+    roof_dec = {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dec_gbs / HBM_PEAK_GBS,
+                "traffic": traffic_for([("decode_qprep", 1), ("decode_partial", 1), ("decode_merge", 1)]),
+                "kernel": "tq_decode_attention call: query prep + split partials + merge",
+                "bytes_per_launch": packed_bytes, "avg_launch_s": d_avg}
+    # quantize: at algorithmic cost the HBM bytes bound it (the two contractions
+    # at bf16 matrix peak take less time than the bytes at HBM peak)
+    roof_q = {"bound": "hbm", "achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+              "frac": q_gbs / HBM_PEAK_GBS, "traffic": traffic_for([("quantize", 2)]),
+              "kernel": "tq_quantize_kv call: K and V launches", "bytes_per_launch": q_bytes,
+              "avg_launch_s": q_avg,
+              "mfma": {"achieved": q_tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": q_tf / BF16_MFMA_PEAK_TFLOPS, "flops_per_launch": q_flops,
+                       "note": "algorithmic 4 d^2 flops per vector; d = 128 executes 6 bf16 passes per "
+                               "vector-pair of contractions (3 for Pi x, 3 for the sketch)"}}
     dominant = roof_q if q_avg >= d_avg else roof_dec
     res = {
         "metric": METRIC, "value": dec_gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": (t1 - t0) / args.steps * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16+i8",
         "data": "synthetic (seeded Gaussian K/V/Q with per-channel scales and outlier channels)",
         "config": {"workload": w.name, "batch": B, "kv_heads": H, "q_heads": w.n_q_heads, "seq_len": T,
                    "head_dim": d, "bits": w.bits, "input_dtype": w.dtype, "rotation_copies": R},
         "decode_pct_hbm_peak": 100 * dec_gbs / HBM_PEAK_GBS,
         "quantize_tokens_per_s": q_tok, "quantize_GBps": q_gbs,
+        "compute": "quantize: bf16-piece MFMA, fp32 accumulate; decode: exact int8 MFMA, int32 "
+                   "accumulate, fp32/fp64 softmax and merge",
         "roofline": dominant, "roofline_decode": roof_dec, "roofline_quantize": roof_q,
         "source_hash": source_hash(),
     }
