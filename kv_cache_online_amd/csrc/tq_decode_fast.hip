@@ -289,12 +289,17 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   constexpr uint32_t kDword3 = 0x00020000u;             // raw buffer, 32-bit data format (gfx9)
   extern __shared__ float sc[];                              // [head][slot in split], base-2 units (S x G)
   __shared__ __attribute__((aligned(16))) unsigned char aw[2][4][4][RB][16][16];  // [part][tile][kgroup][rb][row][byte]
+  // per wave: digit words (weight, residual weight) of its tile in operand byte order
+  __shared__ __attribute__((aligned(16))) uint32_t fst[4][2][RB][4][64];
   __shared__ float redf[4][G];
   __shared__ float redv[4][2];
   __shared__ float mh_s[G];
   __shared__ float lh_s[G];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  // wave index in an SGPR: tile offsets derived from it feed buffer-load SGPR
+  // offsets, which must be provably uniform (else every load becomes a loop)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 15,
+            grp = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   int64_t start, len;
   clip_seq(a, b, &start, &len);
@@ -445,9 +450,15 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
       }
     }
   };
-  for (int tile = wave; tile < ntile; tile += 4) {
-    if (tile != wave) load_k(ka_wd, ka_ws, ka_ksc, ka_vsc, tile);
+  // two register buffers: the next tile's loads are in flight while a tile is scored
+  uint32_t kb_wd[4][3][C], kb_ws[4][C], kb_ksc[4], kb_vsc[4];
+  for (int tile = wave; tile < ntile; tile += 8) {
+    if (tile + 4 < ntile) load_k(kb_wd, kb_ws, kb_ksc, kb_vsc, tile + 4);
     score_k(ka_wd, ka_ws, ka_ksc, ka_vsc, tile);
+    if (tile + 4 < ntile) {
+      if (tile + 8 < ntile) load_k(ka_wd, ka_ws, ka_ksc, ka_vsc, tile + 8);
+      score_k(kb_wd, kb_ws, kb_ksc, kb_vsc, tile + 4);
+    }
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -498,32 +509,46 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
                          int r) {
     const int tile = 4 * r + wave;
     if (tile < ntile) {
+      // weights of this wave's tile: lane (col, grp) takes token nb 16 + col of
+      // head rb 4 + grp; its two digit words go to the wave's staging block at
+      // the token's operand byte position 16 q + 4 sft + i (lane group q of the
+      // value operand, word sft, byte i)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int w64 = nb * 16 + col, t = tile * 64 + w64;
         const bool valid = t >= vlo && t < vhi;
         const float vnu = valid ? f16v(vsc[nb]) : 0.0f, vrho = valid ? f16v(vsc[nb] >> 16) : 0.0f;
-        // token w64 of the tile: 32-slot block w64 >> 5, nibble (w64 & 31) >> 2,
-        // bit w64 & 3 of the nibble -> token group q, operand byte pos, shift
-        const int within = w64 & 31, nib = within >> 2, sft = within & 3;
-        const int q = 2 * (w64 >> 5) + (nib & 1), pos = 4 * sft + (nib >> 1);
+        const int sft = w64 & 3, bi = (w64 >> 3) & 3, q = 2 * (w64 >> 5) + ((w64 >> 2) & 1);
+        const int pos = 16 * q + 4 * sft + bi;
         const float sw = ldexpf(vnu, Ew - sft), swp = ldexpf(vrho, Ewp - sft);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int head = rb * 4 + grp;
-          const float P = valid ? exp2f(sc[head * SMAX + t] - mh[rb]) : 0.0f;
+          const float P = valid ? __builtin_amdgcn_exp2f(sc[head * SMAX + t] - mh[rb]) : 0.0f;
           lloc[rb] += P;
           // truncation toward zero: |error| < 1 unit of 2^-Ew, far below the
           // 24-bit resolution of the float weight itself
-          const uint32_t dw = digits(static_cast<int32_t>(P * sw));
-          const uint32_t dp = digits(static_cast<int32_t>(P * swp));
-#pragma unroll
-          for (int l = 0; l < 4; ++l) {
-            aw[0][tile & 3][q][rb][grp * 4 + l][pos] = static_cast<unsigned char>(dw >> (8 * l));
-            aw[1][tile & 3][q][rb][grp * 4 + l][pos] = static_cast<unsigned char>(dp >> (8 * l));
-          }
+          fst[wave][0][rb][grp][pos] = digits(static_cast<int32_t>(P * sw));
+          fst[wave][1][rb][grp][pos] = digits(static_cast<int32_t>(P * swp));
         }
       }
+      // operand of lane (row col, group grp): row = (head, digit l); word sft
+      // gathers digit l of the four staged words 16 grp + 4 sft + (0..3)
+      const int hd = col >> 2, l = col & 3;
+      const uint32_t sel = uint32_t(l) | (uint32_t(4 + l) << 8) | 0x0C0C0000u;
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int sv = 0; sv < 4; ++sv) {
+            const uint4 f = *reinterpret_cast<const uint4 *>(&fst[wave][x][rb][hd][16 * grp + 4 * sv]);
+            const uint32_t lo = __builtin_amdgcn_perm(f.y, f.x, sel), hi = __builtin_amdgcn_perm(f.w, f.z, sel);
+            wv[sv] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          }
+          *reinterpret_cast<uint4 *>(&aw[x][tile & 3][grp][rb][col][0]) = uint4{wv[0], wv[1], wv[2], wv[3]};
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -552,9 +577,14 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
     }
     __syncthreads();
   };
-  for (int r = 0; r < nround; ++r) {
-    if (r > 0) load_v(va_w, va_s, va_sc, r);
+  uint32_t vb_w[4][3][NB], vb_s[4][NB], vb_sc[4];
+  for (int r = 0; r < nround; r += 2) {
+    if (r + 1 < nround) load_v(vb_w, vb_s, vb_sc, r + 1);
     value_round(va_w, va_s, va_sc, r);
+    if (r + 1 < nround) {
+      if (r + 2 < nround) load_v(va_w, va_s, va_sc, r + 2);
+      value_round(vb_w, vb_s, vb_sc, r + 1);
+    }
   }
 
   // ---- l over the block, then write this split's partial ----
