@@ -283,14 +283,16 @@ template <int D, int RB, int BQK, int BQV>
 __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   constexpr int C = D / 64, W = D / 32, NB = D / 64, G = 4 * RB;
   constexpr int PK = BQK == 3 ? 4 : BQK, PV = BQV == 3 ? 4 : BQV;
-  const int SMAX = a.split_tokens;
+  const int SST = a.split_tokens + 16;  // score row stride: +16 floats spreads 4 heads over the LDS banks
   constexpr int KREC = BQK * W * 4, KSREC = W * 4;      // key bytes per slot: planes, signs
   constexpr int VREC = BQV * D * 4, VSREC = D * 4;      // value bytes per 32-slot block
   constexpr uint32_t kDword3 = 0x00020000u;             // raw buffer, 32-bit data format (gfx9)
-  extern __shared__ float sc[];                              // [head][slot in split], base-2 units (S x G)
-  __shared__ __attribute__((aligned(16))) unsigned char aw[2][4][4][RB][16][16];  // [part][tile][kgroup][rb][row][byte]
-  // per wave: digit words (weight, residual weight) of its tile in operand byte order
-  __shared__ __attribute__((aligned(16))) uint32_t fst[4][2][RB][4][64];
+  extern __shared__ float sc[];                              // [head][slot in split], base-2 units (G x SST)
+  // value A operands of a round: [round parity][part][tile][kgroup][rb][row][byte]; two
+  // rounds' worth, so the next round's writes never meet this round's reads
+  __shared__ __attribute__((aligned(16))) unsigned char aw[2][2][4][4][RB][16][16];
+  // per wave: the digit words of its tile (one part at a time) in operand byte order
+  __shared__ __attribute__((aligned(16))) uint32_t fst[4][RB][4][64];
   __shared__ float redf[4][G];
   __shared__ float redv[4][2];
   __shared__ float mh_s[G];
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
         const float rs = static_cast<float>(fma(2.0, combine(acc_s[rb]), -kcs[rb]));
         float sv = fmaf(knu * al[rb], ri, (krho * be[rb]) * rs);
         sv = valid ? sv : -INFINITY;
-        sc[(rb * 4 + grp) * SMAX + t] = sv;
+        sc[(rb * 4 + grp) * SST + t] = sv;
         mloc[rb] = fmaxf(mloc[rb], sv);
       }
     }
@@ -507,12 +509,14 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   for (int rb = 0; rb < RB; ++rb) lloc[rb] = 0.0f;
   auto value_round = [&](const uint32_t (&vw)[4][3][NB], const uint32_t (&vs)[4][NB], const uint32_t (&vsc)[4],
                          int r) {
-    const int tile = 4 * r + wave;
+    const int tile = 4 * r + wave, par = r & 1;
     if (tile < ntile) {
       // weights of this wave's tile: lane (col, grp) takes token nb 16 + col of
-      // head rb 4 + grp; its two digit words go to the wave's staging block at
-      // the token's operand byte position 16 q + 4 sft + i (lane group q of the
-      // value operand, word sft, byte i)
+      // head rb 4 + grp; its digit words go to the wave's staging block at the
+      // token's operand byte position 16 q + 4 sft + i (lane group q of the
+      // value operand, word sft, byte i): the weight's first, then the
+      // residual weight's
+      uint32_t dres[4][RB];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int w64 = nb * 16 + col, t = tile * 64 + w64;
@@ -524,12 +528,12 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int head = rb * 4 + grp;
-          const float P = valid ? __builtin_amdgcn_exp2f(sc[head * SMAX + t] - mh[rb]) : 0.0f;
+          const float P = valid ? __builtin_amdgcn_exp2f(sc[head * SST + t] - mh[rb]) : 0.0f;
           lloc[rb] += P;
           // truncation toward zero: |error| < 1 unit of 2^-Ew, far below the
           // 24-bit resolution of the float weight itself
-          fst[wave][0][rb][grp][pos] = digits(static_cast<int32_t>(P * sw));
-          fst[wave][1][rb][grp][pos] = digits(static_cast<int32_t>(P * swp));
+          fst[wave][rb][grp][pos] = digits(static_cast<int32_t>(P * sw));
+          dres[nb][rb] = digits(static_cast<int32_t>(P * swp));
         }
       }
       // operand of lane (row col, group grp): row = (head, digit l); word sft
@@ -537,18 +541,30 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
       const int hd = col >> 2, l = col & 3;
       const uint32_t sel = uint32_t(l) | (uint32_t(4 + l) << 8) | 0x0C0C0000u;
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < 2; ++x) {
+        if (x == 1) {
+          // the staged words of part 0 have been read (this wave's LDS operations
+          // complete in order): stage the residual weights in their place
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int w64 = nb * 16 + col;
+            const int pos = 16 * (2 * (w64 >> 5) + ((w64 >> 2) & 1)) + 4 * (w64 & 3) + ((w64 >> 3) & 3);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) fst[wave][rb][grp][pos] = dres[nb][rb];
+          }
+        }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           uint32_t wv[4];
 #pragma unroll
           for (int sv = 0; sv < 4; ++sv) {
-            const uint4 f = *reinterpret_cast<const uint4 *>(&fst[wave][x][rb][hd][16 * grp + 4 * sv]);
+            const uint4 f = *reinterpret_cast<const uint4 *>(&fst[wave][rb][hd][16 * grp + 4 * sv]);
             const uint32_t lo = __builtin_amdgcn_perm(f.y, f.x, sel), hi = __builtin_amdgcn_perm(f.w, f.z, sel);
             wv[sv] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
           }
-          *reinterpret_cast<uint4 *>(&aw[x][tile & 3][grp][rb][col][0]) = uint4{wv[0], wv[1], wv[2], wv[3]};
+          *reinterpret_cast<uint4 *>(&aw[par][x][tile & 3][grp][rb][col][0]) = uint4{wv[0], wv[1], wv[2], wv[3]};
         }
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -557,8 +573,8 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
       v4i aw0[RB], aw1[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        aw0[rb] = *reinterpret_cast<const v4i *>(&aw[0][tt][grp][rb][col][0]);
-        aw1[rb] = *reinterpret_cast<const v4i *>(&aw[1][tt][grp][rb][col][0]);
+        aw0[rb] = *reinterpret_cast<const v4i *>(&aw[par][0][tt][grp][rb][col][0]);
+        aw1[rb] = *reinterpret_cast<const v4i *>(&aw[par][1][tt][grp][rb][col][0]);
         ak[0][rb] = mfma(aw0[rb], ones, ak[0][rb]);
         ak[1][rb] = mfma(aw1[rb], ones, ak[1][rb]);
       }
@@ -575,7 +591,8 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
         for (int rb = 0; rb < RB; ++rb) av[PV][nb][rb] = mfma(aw1[rb], B, av[PV][nb][rb]);
       }
     }
-    __syncthreads();
+    // no barrier here: the next round writes the other parity of aw, and the
+    // round after that is behind the next round's barrier
   };
   uint32_t vb_w[4][3][NB], vb_s[4][NB], vb_sc[4];
   for (int r = 0; r < nround; r += 2) {
@@ -748,7 +765,7 @@ __global__ __launch_bounds__(256) void decode_merge_fast(DecodeArgs a) {
 template <int D, int RB, int BQK>
 int launch_partial_bv(int bqv, const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hkv, a.batch);
-  const size_t lds = size_t(a.split_tokens) * 4 * RB * sizeof(float);  // scores: split x G
+  const size_t lds = size_t(a.split_tokens + 16) * 4 * RB * sizeof(float);  // scores: G x (split + 16)
   switch (bqv) {
     case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1>), grid, dim3(256), lds, s, a); return 0;
     case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2>), grid, dim3(256), lds, s, a); return 0;
