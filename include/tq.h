@@ -116,6 +116,20 @@ typedef struct {
  * 1..3, sigma <= 0 or out == NULL; TQ_ERR_NO_CONVERGENCE after 100000 steps. */
 int tq_build_codebook(int32_t bits_mse, double sigma, tq_codebook *out);
 
+/* Host, pure, reentrant.  The b'-bit Lloyd-Max quantizer of the exact law of
+ * one coordinate of a uniformly random unit vector in R^d, which is the law of
+ * u = Pi x / ||x|| for a random rotation Pi: u^2 ~ Beta(1/2, (d-1)/2), density
+ * (1 - u^2)^((d-3)/2) / B(1/2, (d-1)/2) on [-1, 1].  The method's theory is
+ * stated with beta distributions (kiosknews.app "3 бита вместо 16", section
+ * "Как работает TurboQuant"); the N(0, 1/d) law of tq_build_codebook is its
+ * large-d limit.  Same iteration and
+ * antisymmetrization as tq_build_codebook (stopping when the centroids move
+ * by <= 1e-13 sigma), in absolute u units; sigma is set
+ * to 1/sqrt(d) for reference and mse is the expected squared error per
+ * coordinate under this law.  Returns TQ_ERR_INVALID_ARG for bits_mse outside
+ * 1..3, d < 3 or out == NULL; TQ_ERR_NO_CONVERGENCE after 100000 steps. */
+int tq_build_codebook_sphere(int32_t bits_mse, int32_t d, tq_codebook *out);
+
 /* Per-tensor settings: b' index bits, and whether the 1-bit sign sketch plus
  * ||r|| is stored ([softpro 1.2] stage 2).  Total bits per value b = b' + sketch. */
 typedef struct {

@@ -23,7 +23,7 @@ TQ_LAYOUT_TOKEN_MAJOR, TQ_LAYOUT_BLOCK32 = 0, 1
 TQ_FLAG_NONFINITE_INPUT, TQ_FLAG_SCALE_OVERFLOW, TQ_FLAG_OUT_OF_RANGE = 1, 2, 4
 TQ_MAX_LEVELS = 8
 
-EXPORTED = ("tq_build_codebook", "tq_prepare_bytes", "tq_prepare", "tq_quantize_kv",
+EXPORTED = ("tq_build_codebook", "tq_build_codebook_sphere", "tq_prepare_bytes", "tq_prepare", "tq_quantize_kv",
             "tq_decode_workspace_bytes", "tq_decode_attention", "tq_status_string")
 
 
@@ -63,6 +63,8 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     lib.tq_build_codebook.argtypes = [c_int32, c_double, POINTER(tq_codebook)]
     lib.tq_build_codebook.restype = c_int
+    lib.tq_build_codebook_sphere.argtypes = [c_int32, c_int32, POINTER(tq_codebook)]
+    lib.tq_build_codebook_sphere.restype = c_int
     lib.tq_prepare_bytes.argtypes = [c_int32, c_int32]
     lib.tq_prepare_bytes.restype = c_size_t
     lib.tq_prepare.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p]
@@ -117,6 +119,14 @@ def tq_build_codebook(bits_mse: int, sigma: float) -> tq_codebook:
     return cb
 
 
+def tq_build_codebook_sphere(bits_mse: int, d: int) -> tq_codebook:
+    cb = tq_codebook()
+    st = LIB.tq_build_codebook_sphere(bits_mse, d, ctypes.byref(cb))
+    if st != TQ_OK:
+        raise TQError(st, "tq_build_codebook_sphere")
+    return cb
+
+
 def tq_prepare_bytes(d: int, m: int) -> int:
     return LIB.tq_prepare_bytes(d, m)
 
@@ -153,11 +163,18 @@ def tq_decode_attention(cfg: tq_config, q, dt: int, batch: int, seq_start, seq_l
 
 
 # ------------------------------------------------- struct helpers (host) ---
-def make_spec(bits_mse: int, d: int, sketch: int = 1) -> tq_tensor_spec:
+def make_spec(bits_mse: int, d: int, sketch: int = 1, law: str = "gaussian") -> tq_tensor_spec:
+    """law: "gaussian" (N(0, 1/d), tq_build_codebook) or "sphere" (exact law of a
+    unit-vector coordinate, tq_build_codebook_sphere)."""
     s = tq_tensor_spec()
     s.bits_mse = bits_mse
     s.sketch = sketch
-    s.cb = tq_build_codebook(bits_mse, 1.0 / math.sqrt(d))
+    if law == "gaussian":
+        s.cb = tq_build_codebook(bits_mse, 1.0 / math.sqrt(d))
+    elif law == "sphere":
+        s.cb = tq_build_codebook_sphere(bits_mse, d)
+    else:
+        raise ValueError(f"unknown codebook law {law!r}")
     return s
 
 

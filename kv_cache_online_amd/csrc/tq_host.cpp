@@ -164,6 +164,99 @@ const char *tq_status_string(int s) {
   }
 }
 
+namespace {
+
+// Fill *out from an antisymmetric codebook in absolute units: centroids cs[L],
+// interior boundaries the midpoints, plus fp32 copies and the Walsh
+// expansion over index bit-planes: walsh[S] = mean_i c[i] prod_{p in S} s_p(i).
+// Code L-1-i has every bit of i flipped and c[L-1-i] = -c[i], so the pair
+// (i, L-1-i) cancels for even |S| and doubles for odd |S|.
+void finish_codebook(int bits_mse, double sigma, const double *cs, double mse, int iterations, tq_codebook *out) {
+  const int L = 1 << bits_mse;
+  std::memset(out, 0, sizeof(*out));
+  out->bits_mse = bits_mse;
+  out->levels = L;
+  out->sigma = sigma;
+  for (int k = 0; k < L; ++k) {
+    out->centroid[k] = cs[k];
+    out->centroid_f32[k] = static_cast<float>(cs[k]);
+  }
+  for (int k = 0; k + 1 < L; ++k) {
+    out->boundary[k] = 0.5 * (cs[k] + cs[k + 1]);
+    out->boundary_f32[k] = static_cast<float>(out->boundary[k]);
+  }
+  for (int S = 0; S < L; ++S) {
+    if (!(__builtin_popcount(S) & 1)) {
+      out->walsh[S] = 0.0;
+      continue;
+    }
+    double acc = 0.0;
+    for (int i = 0; i < L / 2; ++i) {
+      double sgn = 1.0;
+      for (int p = 0; p < bits_mse; ++p)
+        if (S >> p & 1) sgn *= (i >> p & 1) ? 1.0 : -1.0;
+      acc += out->centroid[i] * sgn;
+    }
+    out->walsh[S] = 2.0 * acc / L;
+  }
+  out->mse = mse;
+  out->iterations = iterations;
+}
+
+// ------------------------------------------ exact law of one sphere coordinate --
+// A coordinate u of a uniformly random unit vector in R^d (d >= 3) has density
+// (1 - u^2)^((d-3)/2) / B(1/2, (d-1)/2) on [-1, 1]: u^2 ~ Beta(1/2, (d-1)/2).
+
+// Regularized incomplete beta I_x(p, q): prefactor x^p (1-x)^q / (p B(p, q))
+// over the continued fraction 1 + d1/(1 + d2/(1 + ...)) with
+// d_{2m+1} = -(p+m)(p+q+m) x / ((p+2m)(p+2m+1)), d_{2m} = m(q-m) x / ((p+2m-1)(p+2m)),
+// evaluated with the modified Lentz method; past x = (p+1)/(p+q+2), where the
+// fraction converges slowly, through I_x(p, q) = 1 - I_{1-x}(q, p).
+double betainc_reg(double p, double q, double x) {
+  if (x <= 0.0) return 0.0;
+  if (x >= 1.0) return 1.0;
+  if (x > (p + 1.0) / (p + q + 2.0)) return 1.0 - betainc_reg(q, p, 1.0 - x);
+  const double lnpre = p * std::log(x) + q * std::log1p(-x) - std::log(p) -
+                       (std::lgamma(p) + std::lgamma(q) - std::lgamma(p + q));
+  const double tiny = 1e-300;
+  double f = 1.0, C = 1.0, D = 0.0;
+  for (int j = 1; j <= 100000; ++j) {
+    const int m = j / 2;
+    const double dj = (j & 1) ? -(p + m) * (p + q + m) * x / ((p + 2 * m) * (p + 2 * m + 1))
+                              : m * (q - m) * x / ((p + 2 * m - 1) * (p + 2 * m));
+    D = 1.0 + dj * D;
+    if (std::fabs(D) < tiny) D = tiny;
+    D = 1.0 / D;
+    C = 1.0 + dj / C;
+    if (std::fabs(C) < tiny) C = tiny;
+    const double delta = C * D;
+    f *= delta;
+    if (std::fabs(delta - 1.0) < 1e-16) break;
+  }
+  return std::exp(lnpre) / f;
+}
+
+struct SphereLaw {
+  double q;     // (d - 1) / 2
+  double lnB;   // ln B(1/2, q)
+  explicit SphereLaw(int d) : q(0.5 * (d - 1)), lnB(std::lgamma(0.5) + std::lgamma(0.5 * (d - 1)) - std::lgamma(0.5 * d)) {}
+  double tail(double x) const {  // P(u >= x), x >= 0
+    if (x >= 1.0) return 0.0;
+    return 0.5 * betainc_reg(q, 0.5, 1.0 - x * x);
+  }
+  double prob(double a, double b) const {  // P(a < u <= b)
+    if (a >= 0.0) return tail(a) - tail(b);
+    if (b <= 0.0) return tail(-b) - tail(-a);
+    return 1.0 - tail(-a) - tail(b);
+  }
+  double g(double u) const {  // (1 - u^2)^q / (2 q B): int_a^b u f(u) du = g(a) - g(b)
+    if (!(std::fabs(u) < 1.0)) return 0.0;
+    return std::exp(q * std::log1p(-u * u) - std::log(2.0 * q) - lnB);
+  }
+};
+
+}  // namespace
+
 int tq_build_codebook(int32_t bits_mse, double sigma, tq_codebook *out) {
   if (!out || bits_mse < 1 || bits_mse > 3 || !(sigma > 0) || !std::isfinite(sigma))
     return TQ_ERR_INVALID_ARG;
@@ -188,42 +281,46 @@ int tq_build_codebook(int32_t bits_mse, double sigma, tq_codebook *out) {
   if (!done) return TQ_ERR_NO_CONVERGENCE;
   double cs[TQ_MAX_LEVELS];
   for (int k = 0; k < L; ++k) cs[k] = 0.5 * (c[k] - c[L - 1 - k]);  // exact antisymmetry
-  std::memset(out, 0, sizeof(*out));
-  out->bits_mse = bits_mse;
-  out->levels = L;
-  out->sigma = sigma;
   double mse = 1.0;
   t[0] = -INFINITY;
   t[L] = INFINITY;
   for (int k = 1; k < L; ++k) t[k] = 0.5 * (cs[k - 1] + cs[k]);
   for (int k = 0; k < L; ++k) mse -= cell_prob(t[k], t[k + 1]) * cs[k] * cs[k];
-  for (int k = 0; k < L; ++k) {
-    out->centroid[k] = cs[k] * sigma;
-    out->centroid_f32[k] = static_cast<float>(out->centroid[k]);
-  }
-  for (int k = 0; k + 1 < L; ++k) {
-    out->boundary[k] = t[k + 1] * sigma;
-    out->boundary_f32[k] = static_cast<float>(out->boundary[k]);
-  }
-  // Walsh expansion over index bit-planes: walsh[S] = mean_i c[i] prod_{p in S} s_p(i).
-  // Code L-1-i has every bit of i flipped and c[L-1-i] = -c[i], so the pair
-  // (i, L-1-i) cancels for even |S| and doubles for odd |S|.
-  for (int S = 0; S < L; ++S) {
-    if (!(__builtin_popcount(S) & 1)) {
-      out->walsh[S] = 0.0;
-      continue;
+  for (int k = 0; k < L; ++k) cs[k] *= sigma;
+  finish_codebook(bits_mse, sigma, cs, mse * sigma * sigma, it, out);
+  return TQ_OK;
+}
+
+int tq_build_codebook_sphere(int32_t bits_mse, int32_t d, tq_codebook *out) {
+  if (!out || bits_mse < 1 || bits_mse > 3 || d < 3) return TQ_ERR_INVALID_ARG;
+  const int L = 1 << bits_mse;
+  const SphereLaw law(d);
+  const double sigma = 1.0 / std::sqrt(static_cast<double>(d));
+  double c[TQ_MAX_LEVELS], t[TQ_MAX_LEVELS + 1];
+  for (int k = 0; k < L; ++k) c[k] = std::fmax(-0.999, std::fmin(0.999, (2.0 * k - (L - 1)) / L * 2.0 * sigma));
+  int it = 0;
+  bool done = false;
+  for (it = 1; it <= 100000; ++it) {
+    t[0] = -1.0;
+    t[L] = 1.0;
+    for (int k = 1; k < L; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+    double delta = 0.0;
+    for (int k = 0; k < L; ++k) {
+      const double nc = (law.g(t[k]) - law.g(t[k + 1])) / law.prob(t[k], t[k + 1]);
+      delta = std::fmax(delta, std::fabs(nc - c[k]));
+      c[k] = nc;
     }
-    double acc = 0.0;
-    for (int i = 0; i < L / 2; ++i) {
-      double sgn = 1.0;
-      for (int p = 0; p < bits_mse; ++p)
-        if (S >> p & 1) sgn *= (i >> p & 1) ? 1.0 : -1.0;
-      acc += out->centroid[i] * sgn;
-    }
-    out->walsh[S] = 2.0 * acc / L;
+    if (delta <= 1e-13 * sigma) { done = true; break; }  // the beta CDF carries ~1e-15 relative rounding
   }
-  out->mse = mse * sigma * sigma;
-  out->iterations = it;
+  if (!done) return TQ_ERR_NO_CONVERGENCE;
+  double cs[TQ_MAX_LEVELS];
+  for (int k = 0; k < L; ++k) cs[k] = 0.5 * (c[k] - c[L - 1 - k]);
+  double mse = 1.0 / d;  // E[u^2]
+  t[0] = -1.0;
+  t[L] = 1.0;
+  for (int k = 1; k < L; ++k) t[k] = 0.5 * (cs[k - 1] + cs[k]);
+  for (int k = 0; k < L; ++k) mse -= law.prob(t[k], t[k + 1]) * cs[k] * cs[k];
+  finish_codebook(bits_mse, sigma, cs, mse, it, out);
   return TQ_OK;
 }
 

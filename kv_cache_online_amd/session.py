@@ -55,7 +55,7 @@ class PackedCache:
 
 class TQSession:
     def __init__(self, d, n_kv_heads, n_q_heads, rot: np.ndarray, proj: np.ndarray,
-                 k_bits=2, v_bits=2, k_sketch=1, v_sketch=1, device="cuda"):
+                 k_bits=2, v_bits=2, k_sketch=1, v_sketch=1, law="gaussian", device="cuda"):
         self.d, self.n_kv_heads, self.n_q_heads, self.device = d, n_kv_heads, n_q_heads, device
         rot = np.ascontiguousarray(rot, dtype=np.float32)
         proj = np.ascontiguousarray(proj, dtype=np.float32)
@@ -64,8 +64,8 @@ class TQSession:
         self.rot = torch.from_numpy(rot).to(device)
         self.proj = torch.from_numpy(proj).to(device)
         self.prep = torch.from_numpy(blob).to(device)
-        self.k_spec = B.make_spec(k_bits, d, k_sketch)
-        self.v_spec = B.make_spec(v_bits, d, v_sketch)
+        self.k_spec = B.make_spec(k_bits, d, k_sketch, law)
+        self.v_spec = B.make_spec(v_bits, d, v_sketch, law)
         self.cfg = B.make_config(d, n_kv_heads, n_q_heads, self.rot, self.proj, self.prep,
                                  self.k_spec, self.v_spec)
         self.status = torch.zeros(1, dtype=torch.int32, device=device)

@@ -35,7 +35,7 @@ reading kv head h // G.
 Parity status: every function here is pinned by tests in ``tests/test_oracle_*``
 against closed forms, brute force, numerical integration or library routines.
 """
-from .codebook import build_codebook
+from .codebook import build_codebook, build_codebook_sphere
 from .fp16 import fp16_round
 from .quantize import quantize, quantize_conditional
 from .layout import (pack_token_major, unpack_token_major, pack_block32,
@@ -43,6 +43,6 @@ from .layout import (pack_token_major, unpack_token_major, pack_block32,
 from .dequant import dequantize
 from .attention import attention
 
-__all__ = ["build_codebook", "fp16_round", "quantize", "quantize_conditional",
+__all__ = ["build_codebook", "build_codebook_sphere", "fp16_round", "quantize", "quantize_conditional",
            "pack_token_major", "unpack_token_major", "pack_block32", "unpack_block32",
            "record_bytes", "dequantize", "attention"]

@@ -34,7 +34,7 @@ class Run:
     """One workload instance on the device: inputs, caches, quantize, decode."""
 
     def __init__(self, w, batch=None, n_tokens=None, lens=None, k_bits=None, v_bits=None,
-                 k_sketch=None, v_sketch=None, extra=0):
+                 k_sketch=None, v_sketch=None, extra=0, law="gaussian"):
         from kv_cache_online_amd.session import TQSession
         _need_gpu()
         self.w = w
@@ -50,10 +50,14 @@ class Run:
         self.v_sketch = w.sketch if v_sketch is None else v_sketch
         self.rot = W.rotation(w.d, w.wid)
         self.proj = W.sketch(w.m, w.d, w.wid)
-        self.cb_k = O.build_codebook(self.k_bits, 1 / math.sqrt(w.d))
-        self.cb_v = O.build_codebook(self.v_bits, 1 / math.sqrt(w.d))
+        if law == "sphere":
+            self.cb_k = O.build_codebook_sphere(self.k_bits, w.d)
+            self.cb_v = O.build_codebook_sphere(self.v_bits, w.d)
+        else:
+            self.cb_k = O.build_codebook(self.k_bits, 1 / math.sqrt(w.d))
+            self.cb_v = O.build_codebook(self.v_bits, 1 / math.sqrt(w.d))
         self.s = TQSession(w.d, w.n_kv_heads, w.n_q_heads, self.rot, self.proj, k_bits=self.k_bits,
-                           v_bits=self.v_bits, k_sketch=self.k_sketch, v_sketch=self.v_sketch)
+                           v_bits=self.v_bits, k_sketch=self.k_sketch, v_sketch=self.v_sketch, law=law)
         self.kc, self.vc = self.s.new_caches(self.cap)
         self.K = W.kv_batch(w, 0, n_tokens=self.T + extra, batch=self.batch)
         self.V = W.kv_batch(w, 1, n_tokens=self.T + extra, batch=self.batch)
@@ -218,6 +222,18 @@ def test_mse_only_and_asymmetric_bits():
         dbg = run.quantize()
         check_quantize(run, dbg, label=f"k{kb}s{ks}-v{vb}s{vs}")
         check_decode(run, run.decode(), label=f"k{kb}s{ks}-v{vb}s{vs}")
+
+
+@pytest.mark.parametrize("wid,batch,n_tokens", [(2, 1, 400), (3, 1, 300), (5, 1, 257)])
+def test_exact_sphere_law_codebook(wid, batch, n_tokens):
+    """The codebook of the exact unit-vector coordinate law, end to end: the
+    matrix-core quantize and decode (d = 128) and the d = 256 path."""
+    w = W.WORKLOADS[wid]
+    run = Run(w, batch=batch, n_tokens=n_tokens, law="sphere")
+    _log(f"sphere-law codebook, workload {wid}")
+    dbg = run.quantize()
+    check_quantize(run, dbg, label=f"sphere w{wid}")
+    check_decode(run, run.decode(), label=f"sphere w{wid}")
 
 
 # -------------------------------------------------------------- edge cases ---

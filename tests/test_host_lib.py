@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from oracle import build_codebook
+from oracle import build_codebook, build_codebook_sphere
 
 B = pytest.importorskip("kv_cache_online_amd.binding")
 
@@ -65,6 +65,42 @@ def test_codebook_argument_errors():
     for bits, sig in ((0, 0.1), (4, 0.1), (2, 0.0), (2, -1.0), (2, float("nan"))):
         assert B.LIB.tq_build_codebook(bits, sig, ctypes.byref(cb)) == B.TQ_ERR_INVALID_ARG
     assert B.LIB.tq_build_codebook(2, 0.1, None) == B.TQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+@pytest.mark.parametrize("d", [3, 8, 64, 128, 256])
+def test_sphere_codebook_matches_oracle(bits, d):
+    s = 1 / math.sqrt(d)
+    cb = B.tq_build_codebook_sphere(bits, d)
+    ref = build_codebook_sphere(bits, d)
+    L = 1 << bits
+    assert cb.levels == L and cb.bits_mse == bits and abs(cb.sigma - s) < 1e-16
+    # both stop once a step moves the centroids by <= 1e-13 sigma, from different
+    # CDF code; the iteration contracts linearly (rate near 0.95 at 3 bits), so
+    # each can sit ~20 steps' worth from the fixed point: 1e-10 sigma, still
+    # about 1e-3 of an fp32 ulp of the values
+    np.testing.assert_allclose(np.array(cb.centroid[:L]), ref["centroids"], rtol=0, atol=1e-10 * s)
+    np.testing.assert_allclose(np.array(cb.boundary[:L - 1]), ref["boundaries"], rtol=0, atol=1e-10 * s)
+    assert abs(cb.mse - ref["mse"]) <= 1e-10 * ref["mse"]
+    c = np.array(cb.centroid[:L])
+    assert np.all(c == -c[::-1])
+    # Walsh form of this codebook as well
+    for i in range(L):
+        v = 0.0
+        for S in range(L):
+            sg = 1.0
+            for p in range(bits):
+                if S >> p & 1:
+                    sg *= 1.0 if (i >> p) & 1 else -1.0
+            v += cb.walsh[S] * sg
+        assert abs(v - cb.centroid[i]) <= 4 * np.spacing(abs(cb.centroid[i]))  # summation rounding only
+
+
+def test_sphere_codebook_argument_errors():
+    cb = B.tq_codebook()
+    for bits, d in ((0, 128), (4, 128), (2, 2), (2, 0), (2, -5)):
+        assert B.LIB.tq_build_codebook_sphere(bits, d, ctypes.byref(cb)) == B.TQ_ERR_INVALID_ARG
+    assert B.LIB.tq_build_codebook_sphere(2, 128, None) == B.TQ_ERR_INVALID_ARG
 
 
 def _bf16(v):
