@@ -99,7 +99,7 @@ struct DecodeArgs {
   double walsh_k[4];     // key codebook Walsh coefficients, planes ordered s0, s1, s2, s0 s1 s2
   double walsh_v[4];     // value codebook, same order
   void *qop;             // matrix-core A operands of the queries (fast path)
-  double *qconst;        // [batch][Hq][4]: idx correction, sign correction, alpha, beta
+  int32_t *qconst;       // [batch][Hq][8]: index / sign correction as (hi, lo), alpha, beta (fp32 bits), 0, 0
   const void *q;         // [batch][Hq][d]
   int32_t dtype;
   int32_t batch, Hkv, Hq, G;

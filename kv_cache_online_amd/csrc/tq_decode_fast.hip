@@ -71,40 +71,6 @@ __device__ inline uint32_t plane_word(int p, uint32_t w0, uint32_t w1, uint32_t 
   return p == 0 ? w0 : p == 1 ? w1 : p == 2 ? w2 : (w0 ^ w1 ^ w2);
 }
 
-// N consecutive 32-bit words (N = 2 or 4), one vector load.
-template <int N>
-__device__ inline void load_words(const uint32_t *p, uint32_t (&o)[N]) {
-  if constexpr (N == 2) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(p);
-    o[0] = v.x;
-    o[1] = v.y;
-  } else {
-    const uint4 v = *reinterpret_cast<const uint4 *>(p);
-    o[0] = v.x;
-    o[1] = v.y;
-    o[2] = v.z;
-    o[3] = v.w;
-  }
-}
-
-// N consecutive 32-bit words through a buffer descriptor (0 past its end).
-template <int N>
-__device__ inline void buf_words(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t (&o)[N]) {
-  typedef unsigned u2 __attribute__((ext_vector_type(2)));
-  typedef unsigned u4 __attribute__((ext_vector_type(4)));
-  if constexpr (N == 2) {
-    const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-    o[0] = v.x;
-    o[1] = v.y;
-  } else {
-    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    o[0] = v.x;
-    o[1] = v.y;
-    o[2] = v.z;
-    o[3] = v.w;
-  }
-}
-
 __device__ inline v4i mfma(v4i a, v4i b, v4i c) { return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0); }
 
 // sum_l 256^l c_l, exact: every digit sum is below 2^21 in magnitude (operand
@@ -220,7 +186,9 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
                                         (size_t(b * a.Hkv + kvh) * RB + rb) * 5 * C * kWave * 16);
   const int nplane = npk + a.k.sketch;
   double ki = 0.0, ks = 0.0;
-  // entry = (plane, chunk c, lane group g, digit l): 16 bytes for VGPR s, byte i
+  // entry = (plane, chunk c, lane group g, digit l): 16 bytes for VGPR s, byte i.
+  // Lane group g owns plane words g, g + 4, ...; chunk c takes word g + 4 (c >> 1)
+  // and its nibble c & 1: byte i of VGPR s is coordinate 32 (g + 4 (c >> 1)) + 8 i + s + 4 (c & 1).
   for (int e = tid; e < nplane * C * 16; e += 256) {
     const int l = e & 3, g = (e >> 2) & 3, c = (e >> 4) % C, pidx = (e >> 4) / C;
     const bool sign = pidx == npk;
@@ -232,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
     for (int sv = 0; sv < 4; ++sv)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = 32 * ((g >> 1) * C + c) + 8 * i + sv + 4 * (g & 1);
+        const int j = 32 * (g + 4 * (c >> 1)) + 8 * i + sv + 4 * (c & 1);
         const float v = sign ? qs[j] : wk * qr[j];
         const int32_t F = static_cast<int32_t>(rintf(ldexpf(v, E - sv)));
         ksum += int64_t(F) * (int64_t(1) << sv);
@@ -257,18 +225,24 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   }
   __syncthreads();
   if (tid == 0) {
+    // the corrections are integers below 2^53, split as 2^17 hi + lo, 0 <= lo < 2^17
     const double base = double(a.sm_scale) * 1.4426950408889634;  // log2(e): scores in base 2
-    a.qconst[size_t(bh) * 4 + 0] = (wsum[0][0] + wsum[0][1]) + (wsum[0][2] + wsum[0][3]);
-    a.qconst[size_t(bh) * 4 + 1] = (wsum[1][0] + wsum[1][1]) + (wsum[1][2] + wsum[1][3]);
-    a.qconst[size_t(bh) * 4 + 2] = ldexp(base, -Ei);
-    a.qconst[size_t(bh) * 4 + 3] = ldexp(base * double(a.kappa), -Es);
+    const int64_t ki = static_cast<int64_t>((wsum[0][0] + wsum[0][1]) + (wsum[0][2] + wsum[0][3]));
+    const int64_t ks = static_cast<int64_t>((wsum[1][0] + wsum[1][1]) + (wsum[1][2] + wsum[1][3]));
+    int32_t *qc = a.qconst + size_t(bh) * 8;
+    *reinterpret_cast<int4 *>(qc) = make_int4(static_cast<int32_t>(ki >> 17), static_cast<int32_t>(ki & 0x1FFFF),
+                                              static_cast<int32_t>(ks >> 17), static_cast<int32_t>(ks & 0x1FFFF));
+    *reinterpret_cast<int4 *>(qc + 4) =
+        make_int4(__float_as_int(static_cast<float>(ldexp(base, -Ei))),
+                  a.k.sketch ? __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), -Es))) : 0, 0, 0);
   }
 }
 
 // ------------------------------------------------------------ split pass ---
-// One 256-thread block per (split, kv head, sequence).  BQK / BQV: index bits
-// of keys / values (compile time: the plane loops unroll without branches);
-// the sign planes always run, with zero operands when a tensor has no sketch.
+// One 256-thread block per (split, kv head, sequence); a split holds at most
+// kMaxT * 256 slots.  BQK / BQV: index bits of keys / values (compile time: the
+// plane loops unroll without branches); the sign planes always run, with zero
+// operands when a tensor has no sketch.
 //
 // Lane roles: lane = 16 grp + col.  In a score MFMA col is the token of a
 // 16-token block and grp the lane group of the contraction (coordinates); the
@@ -276,21 +250,104 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
 // for that token.  In a value MFMA col is the coordinate of a 16-coordinate
 // block and grp the token group of the contraction.
 //
-// Loads are raw buffer loads: a per-split descriptor (SGPRs) whose size stops
-// at the cache capacity (reads past it return 0), a per-lane constant VGPR
-// offset and a wave-uniform SGPR offset per tile.
+// Data movement: every wave streams its own chunks through a private ring of
+// kSlots LDS slots with buffer loads that write LDS directly (16 bytes per lane,
+// no VGPRs), kSlots - 1 chunks ahead of the one it computes on.  A wave's
+// stream is its key tiles (tiles wave, wave + 4, ...: planes, signs, key and
+// value scales, each a contiguous run of the token-major cache), then one value
+// chunk per round (its quarter of the coordinates of the round's 8 value blocks,
+// one 1 KB load per plane).  Loads complete in order, so a chunk has landed once
+// at most (chunks issued after it) x (fewest loads in a chunk) remain.
+//
+// Scores never leave registers: the lane that scores (head, token) in phase 1
+// is the lane that turns it into a weight in phase 2.
+constexpr int kSlots = 3;  // ring slots per wave
+constexpr int kMaxT = 4;   // key tiles per wave and split: split <= 1024 slots
+
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Raw buffer descriptor (SGPRs): base, no stride, `bytes` records (reads past
+// them return 0), 32-bit data format.
+__device__ inline u4 make_rsrc(const void *base, int bytes) {
+  const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+  u4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(p));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(p >> 32) & 0xFFFFu);
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(bytes));
+  r.w = 0x00020000u;
+  return r;
+}
+
+__device__ inline unsigned lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)p)));
+}
+
+// 16 (or 4) bytes per lane from the buffer straight into LDS at dst + 16 lane
+// (4 lane); dst is wave-uniform (M0).  Every offset goes in the VGPR offset,
+// which the buffer range check covers (the SGPR offset is 0).  Written as asm so that the compiler does
+// not track these loads: it would otherwise wait for all of them before LDS
+// accesses it cannot tell apart from the ring.  The instructions have no
+// register results; the LDS they write is read only after an explicit vmcnt
+// wait (wait_vm), and no load is issued into a slot before this wave's reads
+// of it are complete (lgkmcnt(0) first).
+__device__ inline void dma16(u4 r, unsigned dst, int voff, int soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(dst) : "memory");
+}
+__device__ inline void dma4(u4 r, unsigned dst, int voff, int soff) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(dst) : "memory");
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding.  The
+// memory clobber keeps the compiler from moving LDS reads of the landed chunk
+// above the wait.
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Block barrier for LDS exchanges only: this wave's LDS operations are complete
+// first, but its loads in flight into the ring are not waited for.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ inline uint32_t lds32(const unsigned char *p) { return *reinterpret_cast<const uint32_t *>(p); }
+
+// Score digit sums to 2 x - k exactly, then fp32: x = lo + 2^16 hi with
+// lo = c0 + 2^8 c1, hi = c2 + 2^8 c3, and k = 2^17 KH + KL (0 <= KL < 2^17), so
+// 2 x - k = 2^17 (hi - KH) + (2 lo - KL), both parts exact in int32.
+__device__ inline float score_sum(v4i c, int32_t KH, int32_t KL) {
+  const int32_t lo = c.x + (c.y << 8), hi = c.z + (c.w << 8);
+  return fmaf(static_cast<float>(hi - KH), 131072.0f, static_cast<float>(2 * lo - KL));
+}
+
+template <int D, int RB, int BQK, int BQV>
+struct SplitShape {
+  static constexpr int C = D / 64, W = D / 32, NB = D / 64, NW = D / 128, G = 4 * RB;
+  static constexpr int PK = BQK == 3 ? 4 : BQK, PV = BQV == 3 ? 4 : BQV;
+  static constexpr int KREC = BQK * W * 4, KSREC = W * 4;  // key bytes per slot: planes, signs
+  static constexpr int VREC = BQV * D * 4, VSREC = D * 4;  // value bytes per 32-slot block
+  // key chunk: planes [64][KREC], signs [64][KSREC], key scales [64], value scales [64]
+  static constexpr int K_SG = 64 * KREC, K_KS = K_SG + 64 * KSREC, K_VS = K_KS + 256, K_BYTES = K_VS + 256;
+  // value chunk: [plane (BQV, then signs)][block 8][D / 4 words]
+  static constexpr int VPL = 8 * D, V_BYTES = (BQV + 1) * VPL;
+  static constexpr int SLOT = K_BYTES > V_BYTES ? K_BYTES : V_BYTES;
+  static constexpr int NI_K = (BQK + 1) * NW + 2, NI_V = (BQV + 1) * NW;  // loads per chunk
+  static constexpr int NI_MIN = NI_K < NI_V ? NI_K : NI_V;
+  static constexpr int AWP = RB == 1 ? 2 : 1;  // value operand buffers (round parity)
+};
+
 template <int D, int RB, int BQK, int BQV>
 __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
-  constexpr int C = D / 64, W = D / 32, NB = D / 64, G = 4 * RB;
-  constexpr int PK = BQK == 3 ? 4 : BQK, PV = BQV == 3 ? 4 : BQV;
-  const int SST = a.split_tokens + 16;  // score row stride: +16 floats spreads 4 heads over the LDS banks
-  constexpr int KREC = BQK * W * 4, KSREC = W * 4;      // key bytes per slot: planes, signs
-  constexpr int VREC = BQV * D * 4, VSREC = D * 4;      // value bytes per 32-slot block
-  constexpr uint32_t kDword3 = 0x00020000u;             // raw buffer, 32-bit data format (gfx9)
-  extern __shared__ float sc[];                              // [head][slot in split], base-2 units (G x SST)
-  // value A operands of a round: [round parity][part][tile][kgroup][rb][row][byte]; two
-  // rounds' worth, so the next round's writes never meet this round's reads
-  __shared__ __attribute__((aligned(16))) unsigned char aw[2][2][4][4][RB][16][16];
+  using P = SplitShape<D, RB, BQK, BQV>;
+  constexpr int C = P::C, W = P::W, NB = P::NB, NW = P::NW, G = P::G, PK = P::PK, PV = P::PV;
+  constexpr int KREC = P::KREC, KSREC = P::KSREC, VREC = P::VREC, VSREC = P::VSREC, AWP = P::AWP;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[4][kSlots][P::SLOT];
+  // value A operands of a round: [round parity][part][tile][kgroup][rb][row][byte]
+  __shared__ __attribute__((aligned(16))) unsigned char aw[AWP][2][4][4][RB][16][16];
   // per wave: the digit words of its tile (one part at a time) in operand byte order
   __shared__ __attribute__((aligned(16))) uint32_t fst[4][RB][4][64];
   __shared__ float redf[4][G];
@@ -298,8 +355,8 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   __shared__ float mh_s[G];
   __shared__ float lh_s[G];
 
-  // wave index in an SGPR: tile offsets derived from it feed buffer-load SGPR
-  // offsets, which must be provably uniform (else every load becomes a loop)
+  // wave index in an SGPR: offsets derived from it feed buffer-load SGPR offsets
+  // and the LDS base of the direct loads, which must be provably uniform
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 15,
             grp = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -321,80 +378,65 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   }
   const int ntile = static_cast<int>((hi - abase + 63) >> 6);
   const int vlo = static_cast<int>(lo - abase), vhi = static_cast<int>(hi - abase);  // valid slots
-  const uint32_t sh = (grp & 1) ? 4u : 0u;           // odd nibbles: shift the word right by 4
+  const uint32_t sh = (grp & 1) ? 4u : 0u;  // value operand: odd nibbles, shift the word right by 4
   const uint32_t msk[4] = {0x01010101u, 0x02020202u, 0x04040404u, 0x08080808u};
   const int64_t kcap = a.k.cap, vcap = a.v.cap, vblocks = vcap >> 5;
   const bool skk = a.k.sketch != 0, skv = a.v.sketch != 0;
   const int kslots = static_cast<int>((kcap - abase) < S ? (kcap - abase) : S);
   const int64_t blk0 = abase >> 5;
   const int vblk = static_cast<int>((vblocks - blk0) < (S >> 5) ? (vblocks - blk0) : (S >> 5));
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t *>(a.k.idx + (int64_t(h) * kcap + abase) * BQK * W), 0, kslots * KREC, kDword3);
-  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t *>(skk ? a.k.sgn + (int64_t(h) * kcap + abase) * W : a.k.idx), 0,
-      skk ? kslots * KSREC : 0, kDword3);
-  const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(a.k.scl + (int64_t(h) * kcap + abase) * 2), 0, kslots * 4, kDword3);
+  const u4 rk = make_rsrc(a.k.idx + (int64_t(h) * kcap + abase) * BQK * W, kslots * KREC);
+  const u4 rks = make_rsrc(skk ? a.k.sgn + (int64_t(h) * kcap + abase) * W : a.k.idx, skk ? kslots * KSREC : 0);
+  const u4 rkc = make_rsrc(a.k.scl + (int64_t(h) * kcap + abase) * 2, kslots * 4);
   const int vslots = static_cast<int>((vcap - abase) < S ? (vcap - abase) : S);
-  const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(a.v.scl + (int64_t(h) * vcap + abase) * 2), 0, vslots * 4, kDword3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t *>(a.v.idx + (int64_t(h) * vblocks + blk0) * BQV * D), 0, vblk * VREC, kDword3);
-  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t *>(skv ? a.v.sgn + (int64_t(h) * vblocks + blk0) * D : a.v.idx), 0,
-      skv ? vblk * VSREC : 0, kDword3);
+  const u4 rvc = make_rsrc(a.v.scl + (int64_t(h) * vcap + abase) * 2, vslots * 4);
+  const u4 rv = make_rsrc(a.v.idx + (int64_t(h) * vblocks + blk0) * BQV * D, vblk * VREC);
+  const u4 rvs = make_rsrc(skv ? a.v.sgn + (int64_t(h) * vblocks + blk0) * D : a.v.idx, skv ? vblk * VSREC : 0);
 
-  // ---- loads: one key tile and one value round per register buffer ----
-  const int kvo = col * KREC + (grp >> 1) * C * 4, ksvo = col * KSREC + (grp >> 1) * C * 4;
-  const int j0 = wave * (D / 4) + col * NB;
-  const int vvo = (grp >> 1) * VREC + j0 * 4, vsvo = (grp >> 1) * VSREC + j0 * 4;
-  auto load_k = [&](uint32_t (&wd)[4][3][C], uint32_t (&ws)[4][C], uint32_t (&ksc)[4], uint32_t (&vsc)[4],
-                    int tile) {
+  // ---- the wave's chunk stream ----
+  const int nk = ntile > wave ? (ntile - wave + 3) >> 2 : 0;  // key tiles of this wave
+  const int nr = (ntile + 3) >> 2;                             // value rounds
+  const int nch = nk + nr;
+  // value chunk lane roles: lane -> (block, 16-byte piece) of the wave's coordinates
+  const int vblkl = NW == 1 ? (lane >> 3) : (lane >> 4), vpiece = NW == 1 ? (lane & 7) : (lane & 15);
+  auto issue = [&](int s) {
+    const unsigned dst = lds_addr(&ring[wave][s % kSlots][0]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (s < nk) {
+      const int tile = wave + 4 * s;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int t0 = tile * 64 + nb * 16;  // wave-uniform
+      for (int i = 0; i < BQK * NW; ++i) dma16(rk, dst + 1024 * i, tile * 64 * KREC + 1024 * i + 16 * lane, 0);
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        if (p < BQK) buf_words<C>(rk, kvo + p * W * 4, t0 * KREC, wd[nb][p]);
-        else
+      for (int i = 0; i < NW; ++i) dma16(rks, dst + P::K_SG + 1024 * i, tile * 64 * KSREC + 1024 * i + 16 * lane, 0);
+      dma4(rkc, dst + P::K_KS, tile * 256 + 4 * lane, 0);
+      dma4(rvc, dst + P::K_VS, tile * 256 + 4 * lane, 0);
+    } else {
+      const int r = s - nk;
 #pragma unroll
-          for (int c = 0; c < C; ++c) wd[nb][p][c] = 0u;
-      }
-      buf_words<C>(rks, ksvo, t0 * KSREC, ws[nb]);
-      ksc[nb] = __builtin_amdgcn_raw_buffer_load_b32(rkc, col * 4, t0 * 4, 0);
-      vsc[nb] = __builtin_amdgcn_raw_buffer_load_b32(rvc, col * 4, t0 * 4, 0);
+      for (int p = 0; p <= BQV; ++p)
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+          const bool sg = p == BQV;
+          const int rec = sg ? VSREC : VREC;
+          const int voff = (8 * r + 4 * i + vblkl) * rec + (sg ? 0 : p * D * 4) + wave * D + 16 * vpiece;
+          dma16(sg ? rvs : rv, dst + p * P::VPL + 1024 * i, voff, 0);
+        }
     }
   };
-  // value words of this wave's coordinates for the round's 4 tiles, and the
-  // value scales of the wave's own tile of the round
-  auto load_v = [&](uint32_t (&vw)[4][3][NB], uint32_t (&vs)[4][NB], uint32_t (&vsc)[4], int r) {
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int bl = 2 * (4 * r + tt);  // first 32-slot block of the tile
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        if (p < BQV) buf_words<NB>(rv, vvo + p * D * 4, bl * VREC, vw[tt][p]);
-        else
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) vw[tt][p][nb] = 0u;
-      }
-      buf_words<NB>(rvs, vsvo, bl * VSREC, vs[tt]);
-    }
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      vsc[nb] = __builtin_amdgcn_raw_buffer_load_b32(rvc, col * 4, ((4 * r + wave) * 64 + nb * 16) * 4, 0);
+  auto wait_chunk = [&](int s) {
+    if (s + kSlots - 1 < nch) wait_vm<(kSlots - 1) * P::NI_MIN>();
+    else wait_vm<0>();
   };
 
-  uint32_t ka_wd[4][3][C], ka_ws[4][C], ka_ksc[4], ka_vsc[4];
-  uint32_t va_w[4][3][NB], va_s[4][NB], va_sc[4];
-  const int nround = (ntile + 3) >> 2;
-  load_k(ka_wd, ka_ws, ka_ksc, ka_vsc, wave);   // past the tiles: the descriptor returns 0
-  load_v(va_w, va_s, va_sc, 0);
-
-  // ---- phase 1: scores of this wave's tiles ----
+  // The first kSlots - 1 chunks, then the query operands and constants as plain
+  // loads, which are waited for at once: the compiler does not see the direct
+  // LDS loads, so any wait it placed later for a register load would count too
+  // few loads behind it and drain the ring.  (Issues past the stream read past
+  // the descriptors and land zeros in a free slot.)
+#pragma unroll
+  for (int s = 0; s < kSlots - 1; ++s) issue(s);
   v4i qa[RB][PK + 1][C];
-  double kci[RB], kcs[RB];
-  float al[RB], be[RB];
+  int4 qk[RB], qf[RB];  // per head: correction hi/lo (index, sign), alpha and beta bits
   {
     const v4i *qop = static_cast<const v4i *>(a.qop) + size_t(b * a.Hkv + h) * RB * 5 * C * kWave;
 #pragma unroll
@@ -406,60 +448,77 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
         for (int c = 0; c < C; ++c)
           qa[rb][p][c] = (p < PK || skk) ? qop[((size_t(rb) * 5 + slot) * C + c) * kWave + lane] : v4i{0, 0, 0, 0};
       }
-      const double *qc = a.qconst + size_t(bh0 + rb * 4 + grp) * 4;
-      kci[rb] = qc[0];
-      kcs[rb] = skk ? qc[1] : 0.0;
-      al[rb] = static_cast<float>(qc[2]);
-      be[rb] = skk ? static_cast<float>(qc[3]) : 0.0f;
+      const int4 *qc = reinterpret_cast<const int4 *>(a.qconst + size_t(bh0 + rb * 4 + grp) * 8);
+      qk[rb] = qc[0];
+      qf[rb] = qc[1];
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int p = 0; p <= PK; ++p)
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          asm volatile("" ::"v"(qa[rb][p][c].x), "v"(qa[rb][p][c].y), "v"(qa[rb][p][c].z), "v"(qa[rb][p][c].w));
+      asm volatile("" ::"v"(qk[rb].x), "v"(qk[rb].y), "v"(qk[rb].z), "v"(qk[rb].w), "v"(qf[rb].x), "v"(qf[rb].y));
     }
   }
+
+  // ---- phase 1: scores of this wave's key tiles, kept in registers ----
+  float sreg[kMaxT][4][RB];
+  uint32_t vreg[kMaxT][4];  // value scales of the same tokens, for phase 2
   float mloc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) mloc[rb] = -INFINITY;
   float vnumax = 0.0f, vrhomax = 0.0f;
-  auto score_k = [&](const uint32_t (&wd)[4][3][C], const uint32_t (&ws)[4][C], const uint32_t (&ksc)[4],
-                     const uint32_t (&vsc)[4], int tile) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int t = tile * 64 + nb * 16 + col;
-      const bool valid = t >= vlo && t < vhi;
-      v4i acc_i[RB], acc_s[RB];
+  for (int kt = 0; kt < kMaxT; ++kt) {
+    if (kt < nk) {
+      issue(kt + kSlots - 1);
+      wait_chunk(kt);
+      const unsigned char *sl = &ring[wave][kt % kSlots][0];
+      const int tile = wave + 4 * kt;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) acc_i[rb] = acc_s[rb] = v4i{0, 0, 0, 0};
+      for (int nb = 0; nb < 4; ++nb) {
+        const int tok = nb * 16 + col, t = tile * 64 + tok;
+        const bool valid = t >= vlo && t < vhi;
+        // lane group grp holds words grp, grp + 4, ... of the token's planes
+        uint32_t wd[3][NW], ws[NW];
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
+        for (int u = 0; u < NW; ++u) {
 #pragma unroll
-        for (int p = 0; p < PK; ++p) {
-          const v4i B = expand(plane_word<4>(p, wd[nb][0][c], wd[nb][1][c], wd[nb][2][c]), sh, msk);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc_i[rb] = mfma(qa[rb][p][c], B, acc_i[rb]);
+          for (int p = 0; p < 3; ++p) wd[p][u] = p < BQK ? lds32(sl + tok * KREC + p * W * 4 + (grp + 4 * u) * 4) : 0u;
+          ws[u] = lds32(sl + P::K_SG + tok * KSREC + (grp + 4 * u) * 4);
         }
-        const v4i B = expand(ws[nb][c], sh, msk);
+        const uint32_t ksc = lds32(sl + P::K_KS + 4 * tok), vsc = lds32(sl + P::K_VS + 4 * tok);
+        v4i acc_i[RB], acc_s[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc_s[rb] = mfma(qa[rb][PK][c], B, acc_s[rb]);
-      }
-      const float knu = f16v(ksc[nb]), krho = f16v(ksc[nb] >> 16);
-      vnumax = fmaxf(vnumax, valid ? f16v(vsc[nb]) : 0.0f);
-      vrhomax = fmaxf(vrhomax, valid ? f16v(vsc[nb] >> 16) : 0.0f);
+        for (int rb = 0; rb < RB; ++rb) acc_i[rb] = acc_s[rb] = v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float ri = static_cast<float>(fma(2.0, combine(acc_i[rb]), -kci[rb]));
-        const float rs = static_cast<float>(fma(2.0, combine(acc_s[rb]), -kcs[rb]));
-        float sv = fmaf(knu * al[rb], ri, (krho * be[rb]) * rs);
-        sv = valid ? sv : -INFINITY;
-        sc[(rb * 4 + grp) * SST + t] = sv;
-        mloc[rb] = fmaxf(mloc[rb], sv);
+        for (int c = 0; c < C; ++c) {
+#pragma unroll
+          for (int p = 0; p < PK; ++p) {
+            const v4i B = expand(plane_word<4>(p, wd[0][c >> 1], wd[1][c >> 1], wd[2][c >> 1]), 4u * (c & 1), msk);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) acc_i[rb] = mfma(qa[rb][p][c], B, acc_i[rb]);
+          }
+          const v4i B = expand(ws[c >> 1], 4u * (c & 1), msk);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc_s[rb] = mfma(qa[rb][PK][c], B, acc_s[rb]);
+        }
+        const float knu = f16v(ksc), krho = f16v(ksc >> 16);
+        vreg[kt][nb] = vsc;
+        vnumax = fmaxf(vnumax, valid ? f16v(vsc) : 0.0f);
+        vrhomax = fmaxf(vrhomax, valid ? f16v(vsc >> 16) : 0.0f);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float ri = score_sum(acc_i[rb], qk[rb].x, qk[rb].y);
+          const float rs = score_sum(acc_s[rb], qk[rb].z, qk[rb].w);
+          float sv = fmaf(knu * __int_as_float(qf[rb].x), ri, (krho * __int_as_float(qf[rb].y)) * rs);
+          sv = valid ? sv : -INFINITY;
+          sreg[kt][nb][rb] = sv;
+          mloc[rb] = fmaxf(mloc[rb], sv);
+        }
       }
-    }
-  };
-  // two register buffers: the next tile's loads are in flight while a tile is scored
-  uint32_t kb_wd[4][3][C], kb_ws[4][C], kb_ksc[4], kb_vsc[4];
-  for (int tile = wave; tile < ntile; tile += 8) {
-    if (tile + 4 < ntile) load_k(kb_wd, kb_ws, kb_ksc, kb_vsc, tile + 4);
-    score_k(ka_wd, ka_ws, ka_ksc, ka_vsc, tile);
-    if (tile + 4 < ntile) {
-      if (tile + 8 < ntile) load_k(ka_wd, ka_ws, ka_ksc, ka_vsc, tile + 8);
-      score_k(kb_wd, kb_ws, kb_ksc, kb_vsc, tile + 4);
     }
   }
 #pragma unroll
@@ -478,12 +537,12 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
     redv[wave][0] = vnumax;
     redv[wave][1] = vrhomax;
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < G) mh_s[tid] = fmaxf(fmaxf(redf[0][tid], redf[1][tid]), fmaxf(redf[2][tid], redf[3][tid]));
   const float vn_all = fmaxf(fmaxf(redv[0][0], redv[1][0]), fmaxf(redv[2][0], redv[3][0]));
   const float vr_all = fmaxf(fmaxf(redv[0][1], redv[1][1]), fmaxf(redv[2][1], redv[3][1]));
   const int Ew = fix_exp(vn_all), Ewp = fix_exp(vr_all);
-  __syncthreads();
+  lds_barrier();
   float mh[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) mh[rb] = mh_s[rb * 4 + grp];
@@ -507,100 +566,125 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   float lloc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) lloc[rb] = 0.0f;
-  auto value_round = [&](const uint32_t (&vw)[4][3][NB], const uint32_t (&vs)[4][NB], const uint32_t (&vsc)[4],
-                         int r) {
-    const int tile = 4 * r + wave, par = r & 1;
-    if (tile < ntile) {
-      // weights of this wave's tile: lane (col, grp) takes token nb 16 + col of
-      // head rb 4 + grp; its digit words go to the wave's staging block at the
-      // token's operand byte position 16 q + 4 sft + i (lane group q of the
-      // value operand, word sft, byte i): the weight's first, then the
-      // residual weight's
-      uint32_t dres[4][RB];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int w64 = nb * 16 + col, t = tile * 64 + w64;
-        const bool valid = t >= vlo && t < vhi;
-        const float vnu = valid ? f16v(vsc[nb]) : 0.0f, vrho = valid ? f16v(vsc[nb] >> 16) : 0.0f;
-        const int sft = w64 & 3, bi = (w64 >> 3) & 3, q = 2 * (w64 >> 5) + ((w64 >> 2) & 1);
-        const int pos = 16 * q + 4 * sft + bi;
-        const float sw = ldexpf(vnu, Ew - sft), swp = ldexpf(vrho, Ewp - sft);
+  for (int r = 0; r < kMaxT; ++r) {
+    if (r < nr) {
+      const int s = nk + r, par = AWP == 2 ? (r & 1) : 0;
+      if (s + kSlots - 1 < nch) issue(s + kSlots - 1);
+      if (r < nk) {
+        // weights of this wave's tile 4 r + wave (its key tile r): lane (col, grp)
+        // takes token nb 16 + col of head rb 4 + grp; its digit words go to the
+        // wave's staging block at the token's operand byte position 16 q + 4 sft + i
+        // (lane group q of the value operand, word sft, byte i): the weight's
+        // first, then the residual weight's
+        const int tile = 4 * r + wave;
+        uint32_t dres[4][RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int head = rb * 4 + grp;
-          const float P = valid ? __builtin_amdgcn_exp2f(sc[head * SST + t] - mh[rb]) : 0.0f;
-          lloc[rb] += P;
-          // truncation toward zero: |error| < 1 unit of 2^-Ew, far below the
-          // 24-bit resolution of the float weight itself
-          fst[wave][rb][grp][pos] = digits(static_cast<int32_t>(P * sw));
-          dres[nb][rb] = digits(static_cast<int32_t>(P * swp));
+        for (int nb = 0; nb < 4; ++nb) {
+          const int w64 = nb * 16 + col, t = tile * 64 + w64;
+          const bool valid = t >= vlo && t < vhi;
+          const float vnu = valid ? f16v(vreg[r][nb]) : 0.0f, vrho = valid ? f16v(vreg[r][nb] >> 16) : 0.0f;
+          const int sft = w64 & 3, bi = (w64 >> 3) & 3, q = 2 * (w64 >> 5) + ((w64 >> 2) & 1);
+          const int pos = 16 * q + 4 * sft + bi;
+          const float sw = ldexpf(vnu, Ew - sft), swp = ldexpf(vrho, Ewp - sft);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const float Pw = valid ? __builtin_amdgcn_exp2f(sreg[r][nb][rb] - mh[rb]) : 0.0f;
+            lloc[rb] += Pw;
+            // truncation toward zero: |error| < 1 unit of 2^-Ew, far below the
+            // 24-bit resolution of the float weight itself
+            fst[wave][rb][grp][pos] = digits(static_cast<int32_t>(Pw * sw));
+            dres[nb][rb] = digits(static_cast<int32_t>(Pw * swp));
+          }
+        }
+        // operand of lane (row col, group grp): row = (head, digit l); word sft
+        // gathers digit l of the four staged words 16 grp + 4 sft + (0..3)
+        const int hd = col >> 2, l = col & 3;
+        const uint32_t sel = uint32_t(l) | (uint32_t(4 + l) << 8) | 0x0C0C0000u;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          if (x == 1) {
+            // the staged words of part 0 have been read (this wave's LDS operations
+            // complete in order): stage the residual weights in their place
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              const int w64 = nb * 16 + col;
+              const int pos = 16 * (2 * (w64 >> 5) + ((w64 >> 2) & 1)) + 4 * (w64 & 3) + ((w64 >> 3) & 3);
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb) fst[wave][rb][grp][pos] = dres[nb][rb];
+            }
+          }
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            uint32_t wv[4];
+#pragma unroll
+            for (int sv = 0; sv < 4; ++sv) {
+              const uint4 f = *reinterpret_cast<const uint4 *>(&fst[wave][rb][hd][16 * grp + 4 * sv]);
+              const uint32_t lo2 = __builtin_amdgcn_perm(f.y, f.x, sel), hi2 = __builtin_amdgcn_perm(f.w, f.z, sel);
+              wv[sv] = __builtin_amdgcn_perm(hi2, lo2, 0x05040100u);
+            }
+            *reinterpret_cast<uint4 *>(&aw[par][x][wave][grp][rb][col][0]) = uint4{wv[0], wv[1], wv[2], wv[3]};
+          }
         }
       }
-      // operand of lane (row col, group grp): row = (head, digit l); word sft
-      // gathers digit l of the four staged words 16 grp + 4 sft + (0..3)
-      const int hd = col >> 2, l = col & 3;
-      const uint32_t sel = uint32_t(l) | (uint32_t(4 + l) << 8) | 0x0C0C0000u;
+      lds_barrier();
+      wait_chunk(s);
+      const unsigned char *sl = &ring[wave][s % kSlots][0];
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        if (x == 1) {
-          // the staged words of part 0 have been read (this wave's LDS operations
-          // complete in order): stage the residual weights in their place
+      for (int tt = 0; tt < 4; ++tt) {
+        if (4 * r + tt >= ntile) break;
+        v4i aw0[RB], aw1[RB];
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            const int w64 = nb * 16 + col;
-            const int pos = 16 * (2 * (w64 >> 5) + ((w64 >> 2) & 1)) + 4 * (w64 & 3) + ((w64 >> 3) & 3);
+        for (int rb = 0; rb < RB; ++rb) {
+          aw0[rb] = *reinterpret_cast<const v4i *>(&aw[par][0][tt][grp][rb][col][0]);
+          aw1[rb] = *reinterpret_cast<const v4i *>(&aw[par][1][tt][grp][rb][col][0]);
+          ak[0][rb] = mfma(aw0[rb], ones, ak[0][rb]);
+          ak[1][rb] = mfma(aw1[rb], ones, ak[1][rb]);
+        }
+        // words of coordinates col NB .. col NB + NB - 1 (of the wave's quarter) in
+        // value block 2 tt + grp / 2 of the round
+        const unsigned char *vb = sl + (2 * tt + (grp >> 1)) * D + col * NB * 4;
+        uint32_t vw[3][NB], vs[NB];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) fst[wave][rb][grp][pos] = dres[nb][rb];
+        for (int p = 0; p <= BQV; ++p) {
+          uint32_t t4[NB];
+          if constexpr (NB == 2) {
+            const uint2 v2 = *reinterpret_cast<const uint2 *>(vb + p * P::VPL);
+            t4[0] = v2.x;
+            t4[1] = v2.y;
+          } else {
+            const uint4 v4 = *reinterpret_cast<const uint4 *>(vb + p * P::VPL);
+            t4[0] = v4.x;
+            t4[1] = v4.y;
+            t4[2] = v4.z;
+            t4[3] = v4.w;
+          }
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            if (p == BQV) vs[nb] = t4[nb];
+            else vw[p][nb] = t4[nb];
           }
         }
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          uint32_t wv[4];
+        for (int p = BQV; p < 3; ++p)
 #pragma unroll
-          for (int sv = 0; sv < 4; ++sv) {
-            const uint4 f = *reinterpret_cast<const uint4 *>(&fst[wave][rb][hd][16 * grp + 4 * sv]);
-            const uint32_t lo = __builtin_amdgcn_perm(f.y, f.x, sel), hi = __builtin_amdgcn_perm(f.w, f.z, sel);
-            wv[sv] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          for (int nb = 0; nb < NB; ++nb) vw[p][nb] = 0u;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int p = 0; p < PV; ++p) {
+            const v4i B = expand(plane_word<4>(p, vw[0][nb], vw[1][nb], vw[2][nb]), sh, msk);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) av[p][nb][rb] = mfma(aw0[rb], B, av[p][nb][rb]);
           }
-          *reinterpret_cast<uint4 *>(&aw[par][x][tile & 3][grp][rb][col][0]) = uint4{wv[0], wv[1], wv[2], wv[3]};
+          const v4i B = expand(vs[nb], sh, msk);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) av[PV][nb][rb] = mfma(aw1[rb], B, av[PV][nb][rb]);
         }
       }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (4 * r + tt >= ntile) break;
-      v4i aw0[RB], aw1[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        aw0[rb] = *reinterpret_cast<const v4i *>(&aw[par][0][tt][grp][rb][col][0]);
-        aw1[rb] = *reinterpret_cast<const v4i *>(&aw[par][1][tt][grp][rb][col][0]);
-        ak[0][rb] = mfma(aw0[rb], ones, ak[0][rb]);
-        ak[1][rb] = mfma(aw1[rb], ones, ak[1][rb]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int p = 0; p < PV; ++p) {
-          const v4i B = expand(plane_word<4>(p, vw[tt][0][nb], vw[tt][1][nb], vw[tt][2][nb]), sh, msk);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) av[p][nb][rb] = mfma(aw0[rb], B, av[p][nb][rb]);
-        }
-        const v4i B = expand(vs[tt][nb], sh, msk);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) av[PV][nb][rb] = mfma(aw1[rb], B, av[PV][nb][rb]);
-      }
-    }
-    // no barrier here: the next round writes the other parity of aw, and the
-    // round after that is behind the next round's barrier
-  };
-  uint32_t vb_w[4][3][NB], vb_s[4][NB], vb_sc[4];
-  for (int r = 0; r < nround; r += 2) {
-    if (r + 1 < nround) load_v(vb_w, vb_s, vb_sc, r + 1);
-    value_round(va_w, va_s, va_sc, r);
-    if (r + 1 < nround) {
-      if (r + 2 < nround) load_v(va_w, va_s, va_sc, r + 2);
-      value_round(vb_w, vb_s, vb_sc, r + 1);
+      // with two operand buffers the next round writes the other one, and the
+      // round after that is behind the next round's barrier; with one, wait here
+      if (AWP == 1) lds_barrier();
     }
   }
 
@@ -612,9 +696,10 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   if (col == 0)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) redf[wave][rb * 4 + grp] = lloc[rb];
-  __syncthreads();
+  lds_barrier();
   if (tid < G) lh_s[tid] = (redf[0][tid] + redf[1][tid]) + (redf[2][tid] + redf[3][tid]);
-  __syncthreads();
+  lds_barrier();
+  const int j0 = wave * (D / 4) + col * NB;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int head = rb * 4 + grp;
@@ -765,11 +850,11 @@ __global__ __launch_bounds__(256) void decode_merge_fast(DecodeArgs a) {
 template <int D, int RB, int BQK>
 int launch_partial_bv(int bqv, const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hkv, a.batch);
-  const size_t lds = size_t(a.split_tokens + 16) * 4 * RB * sizeof(float);  // scores: G x (split + 16)
+  if (a.split_tokens > kMaxT * 256) return 1;
   switch (bqv) {
-    case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1>), grid, dim3(256), lds, s, a); return 0;
-    case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2>), grid, dim3(256), lds, s, a); return 0;
-    case 3: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 3>), grid, dim3(256), lds, s, a); return 0;
+    case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1>), grid, dim3(256), 0, s, a); return 0;
+    case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2>), grid, dim3(256), 0, s, a); return 0;
+    case 3: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 3>), grid, dim3(256), 0, s, a); return 0;
     default: return 1;
   }
 }

@@ -121,14 +121,13 @@ DecodePlan decode_plan(const tq_config &cfg, int32_t batch, int32_t max_len) {
   const int G = cfg.n_kv_heads > 0 ? cfg.n_q_heads / cfg.n_kv_heads : 1;
   p.fast = (cfg.d == 128 || cfg.d == 256) && (G == 4 || G == 8);
   p.rb = G >= 4 ? G / 4 : 1;
-  // Split length: a multiple of 256 slots (4 waves x 64), sized for about 2048
-  // work-groups, and capped so that the split's scores (split x G floats) stay
-  // within 32 KB of LDS.
+  // Split length: a multiple of 256 slots (4 waves x 64), sized for about 512
+  // work-groups (two per CU), at most 1024 slots (four key tiles per wave, whose
+  // scores the split pass keeps in registers).
   const int64_t pairs = int64_t(batch) * cfg.n_kv_heads;
-  int64_t st = pairs > 0 ? (int64_t(max_len) * pairs + 2047) / 2048 : 256;
+  int64_t st = pairs > 0 ? (int64_t(max_len) * pairs + 511) / 512 : 256;
   st = (st + 255) / 256 * 256;
-  const int64_t cap = (8192 / (G > 0 ? G : 1)) / 256 * 256;
-  if (st > cap) st = cap;
+  if (st > 1024) st = 1024;
   if (st < 256) st = 256;
   p.split_tokens = static_cast<int32_t>(st);
   // Splits are aligned to absolute 64-slot tiles, so a sequence may start up to 63
@@ -488,7 +487,7 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
   a.split_tokens = p.split_tokens;
   a.n_split = p.n_split;
   a.qop = ws + p.off_qop;
-  a.qconst = reinterpret_cast<double *>(ws + p.off_qconst);
+  a.qconst = reinterpret_cast<int32_t *>(ws + p.off_qconst);
   for (int t = 0; t < 2; ++t) {
     const tq_codebook &cb = t ? cfg->v.cb : cfg->k.cb;
     double *wc = t ? a.walsh_v : a.walsh_k;
