@@ -107,17 +107,20 @@ __device__ inline void clip_seq(const DecodeArgs &a, int b, int64_t *start, int6
 
 // ------------------------------------------------------------- query prep ---
 // One block per (sequence, query head): q_rot = Pi q and q_s = S q in fp32
-// (one matrix row per thread, the row's loads issued together; the products
-// carry about 2^-24 relative error, far inside what the scores need), then this
-// head's four rows (one per digit) of every score operand, written as 16-byte
-// lane entries, and the exact correction constants sum_j F_j 2^shift_j.
-// Reductions run on wave shuffles, so the block needs four barriers.
+// (the products carry about 2^-24 relative error, far inside what the scores
+// need), then this head's four rows (one per digit) of every score operand,
+// written as 16-byte lane entries, and the exact correction constants
+// sum_j F_j 2^shift_j.
+// The contraction reads the transposed matrices [Pi^T | S^T] (k rows, 2D
+// columns) so that a wave's loads are contiguous: thread (kg, cg) sums rows
+// k in its k-group for the four columns 4 cg .. 4 cg + 3, its first chunk of
+// loads issued before q arrives; the k-groups are then added in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   constexpr int C = D / 64;
-  constexpr int RPT = 2 * D / 256;  // matrix rows per thread (rows 0..D-1: Pi, D..2D-1: S)
-  constexpr int CH = 32 / RPT;      // float4 loads in flight per row chunk
+  constexpr int NCG = 2 * D / 4, NKG = 256 / NCG, KPER = D / NKG, CH = 32;  // column / k groups
   __shared__ __attribute__((aligned(16))) float q[D];
+  __shared__ __attribute__((aligned(16))) float part[NKG][2 * D];
   __shared__ float qr[D], qs[D];
   __shared__ float wmax[2][4];
   __shared__ double wsum[2][4];
@@ -125,44 +128,46 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   const int bh = blockIdx.x, b = bh / a.Hq, hq = bh % a.Hq;
   const int kvh = hq / a.G, hl = hq % a.G, rb = hl >> 2, row0 = (hl & 3) * 4;
   const int RB = a.G / 4;
-  // the matrix rows do not depend on q: issue their first chunk before q arrives
-  float4 m0[RPT][CH];
+  const int cg = tid % NCG, kg = tid / NCG;
+  const bool isr = 4 * cg < D;
+  const float *mt = isr ? a.rotT + 4 * cg : a.projT + (4 * cg - D);  // column block of row 0
+  const int k0 = kg * KPER;
+  float4 m[CH];
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const int r = tid + 256 * u;
-    const float4 *row = reinterpret_cast<const float4 *>((r < D ? a.rot : a.proj) + size_t(r < D ? r : r - D) * D);
-#pragma unroll
-    for (int k = 0; k < CH; ++k) m0[u][k] = row[k];
-  }
+  for (int k = 0; k < CH; ++k) m[k] = *reinterpret_cast<const float4 *>(mt + size_t(k0 + k) * D);
   for (int j = tid; j < D; j += 256) q[j] = load_q(a.q, a.dtype, size_t(bh) * D + j);
   __syncthreads();
-  float mr = 0.0f, ms = 0.0f;
+  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 1
+  for (int kc = 0; kc < KPER; kc += CH) {
+    if (kc > 0)
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const int r = tid + 256 * u;
-    const bool isr = r < D;
-    const float4 *row = reinterpret_cast<const float4 *>((isr ? a.rot : a.proj) + size_t(isr ? r : r - D) * D);
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int k = 0; k < CH; ++k) m[k] = *reinterpret_cast<const float4 *>(mt + size_t(k0 + kc + k) * D);
 #pragma unroll
-    for (int k0 = 0; k0 < D / 4; k0 += CH) {
-      float4 m[CH];
+    for (int k = 0; k < CH; k += 4) {
+      const float4 x = *reinterpret_cast<const float4 *>(&q[k0 + kc + k]);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-      for (int k = 0; k < CH; ++k) m[k] = k0 == 0 ? m0[u][k] : row[k0 + k];
-#pragma unroll
-      for (int k = 0; k < CH; ++k) {
-        const float4 x = *reinterpret_cast<const float4 *>(&q[4 * (k0 + k)]);
-        acc[0] = fmaf(m[k].x, x.x, acc[0]);
-        acc[1] = fmaf(m[k].y, x.y, acc[1]);
-        acc[2] = fmaf(m[k].z, x.z, acc[2]);
-        acc[3] = fmaf(m[k].w, x.w, acc[3]);
+      for (int u = 0; u < 4; ++u) {
+        acc.x = fmaf(m[k + u].x, xv[u], acc.x);
+        acc.y = fmaf(m[k + u].y, xv[u], acc.y);
+        acc.z = fmaf(m[k + u].z, xv[u], acc.z);
+        acc.w = fmaf(m[k + u].w, xv[u], acc.w);
       }
     }
-    const float v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    if (isr) {
-      qr[r] = v;
+  }
+  *reinterpret_cast<float4 *>(&part[kg][4 * cg]) = acc;
+  __syncthreads();
+  float mr = 0.0f, ms = 0.0f;
+  for (int c = tid; c < 2 * D; c += 256) {
+    float v = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NKG; ++g) v += part[g][c];
+    if (c < D) {
+      qr[c] = v;
       mr = fmaxf(mr, fabsf(v));
     } else {
-      qs[r - D] = v;
+      qs[c - D] = v;
       ms = fmaxf(ms, fabsf(v));
     }
   }
