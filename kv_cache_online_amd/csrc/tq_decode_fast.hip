@@ -725,137 +725,136 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
 }
 
 // ----------------------------------------------------------------- merge ---
-// One block per (sequence, query head): log-sum-exp merge of the split
-// partials, then out = (Pi^T A + kappa S^T B) / l.
-// Thread (sg, eg), sg = tid / 16, eg = tid % 16, merges splits sg, sg + 16, ...
-// for the EPT consecutive elements eg * EPT of (A, B) with a running maximum,
-// loading NBT splits at a time before using any of them; the 16 split groups
-// are then combined in LDS.  A split with no tokens (l = 0) has unwritten A, B
-// and is skipped.  The projection tiles k across 256 / (D / 4) thread groups.
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_fast(DecodeArgs a) {
-  constexpr int EPT = 2 * D / 16;  // elements of (A, B) per thread
-  constexpr int NBT = D == 128 ? 4 : 2;
-  constexpr int JG = D / 4, KG = 256 / JG, KPER = D / KG, KCH = 16;
-  __shared__ __attribute__((aligned(16))) float part_s[16][2 * D];
-  __shared__ float ms_s[16], ls_s[16];
-  __shared__ __attribute__((aligned(16))) float AB[2 * D];
-  __shared__ __attribute__((aligned(16))) float prj[KG][D];
-  const int tid = threadIdx.x, sg = tid >> 4, eg = tid & 15;
-  const size_t bh = blockIdx.x;
+// out = (Pi^T A + kappa S^T B) / l, where (A, B) and l merge the split partials
+// by log-sum-exp.  Block (head, cs) computes the CPB x 64 outputs from 64 CPB cs
+// on (CPB = d / 64, one block per head, when there are heads enough to fill the
+// chip; else CPB = 1):
+//  1. the split maxima and sums: M = max m_s over splits with tokens, weights
+//     w_s = exp(m_s - M) (0 for a split with no tokens, whose (A, B) are
+//     unwritten), l = sum w_s l_s; the weights go to LDS.
+//  2. thread (sg, e) sums w_s x_s for element e of (A, B) over splits sg,
+//     sg + SGN, ...; its loads are issued before step 1 (they do not depend on
+//     the weights), as are the matrix loads of step 3.  The split groups are
+//     added in LDS.
+//  3. per group of 64 columns, thread (kq, jj) takes rows kq, kq + 8, ... of
+//     [Pi ; S] (2 d rows) at the group's column jj; the 8 row groups are added
+//     in LDS.
+// Every block of a head recomputes steps 1-2 so that no block waits on another.
+constexpr int kMaxSplits = 2048;
+
+template <int D, int CPB>
+__global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
+  constexpr int NT = 512, SGN = NT / (2 * D), CHS = 32;  // split groups, split loads per chunk
+  constexpr int RPT = 2 * D / 8;                         // matrix rows per thread
+  __shared__ float ws_l[kMaxSplits], ls_l[kMaxSplits];
+  __shared__ float red[8];
+  __shared__ float accg[SGN][2 * D];
+  __shared__ float prj[8][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int ncs = D / (64 * CPB);
+  const int bh = blockIdx.x / ncs, cs = blockIdx.x % ncs;
   const int stride = 2 + 2 * D, ns = a.n_split;
-  const float *base = a.part + bh * ns * stride;
-  // the projection rows of the first chunk do not depend on the partials:
-  // issue them first
-  const int jg = tid % JG, kg = tid / JG;
-  const bool skv = a.v.sketch != 0;
-  float4 r0[KCH], sp0[KCH];
+  const float *base = a.part + size_t(bh) * ns * stride;
+  // step 3's matrix column: rows kq + 8 i of [Pi ; S]
+  const int jj = tid & 63, kq = tid >> 6;
+  float mrow[RPT];
+  auto load_rows = [&](int col) {
 #pragma unroll
-  for (int kk = 0; kk < KCH; ++kk) {
-    const int k = kg * KPER + kk;
-    r0[kk] = *reinterpret_cast<const float4 *>(a.rot + size_t(k) * D + 4 * jg);
-    sp0[kk] = skv ? *reinterpret_cast<const float4 *>(a.proj + size_t(k) * D + 4 * jg) : float4{0, 0, 0, 0};
-  }
-  float m_run = -INFINITY, l_run = 0.0f;
-  float acc[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) acc[e] = 0.0f;
-  for (int s0 = sg; s0 < ns; s0 += 16 * NBT) {
-    float pm[NBT], pl[NBT];
-    float2 x[NBT][EPT / 2];
-#pragma unroll
-    for (int u = 0; u < NBT; ++u) {
-      const int s = s0 + 16 * u;
-      pm[u] = -INFINITY;
-      pl[u] = 0.0f;
-      if (s < ns) {
-        const float *p = base + size_t(s) * stride;
-        pm[u] = p[0];
-        pl[u] = p[1];
-        // records are 2 + 2D floats: element 2 + e sits 8 bytes past a 16-byte
-        // boundary, so read as float2 pairs
-        const float2 *q = reinterpret_cast<const float2 *>(p + 2 + eg * EPT);
-#pragma unroll
-        for (int e = 0; e < EPT / 2; ++e) x[u][e] = q[e];
-      }
+    for (int i = 0; i < RPT; ++i) {
+      const int k = kq + 8 * i;
+      mrow[i] = k < D ? a.rot[size_t(k) * D + col] : a.proj[size_t(k - D) * D + col];
     }
+  };
+  load_rows(64 * CPB * cs + jj);
+  // step 2's first chunk of elements
+  const int e = tid % (2 * D), sg = tid / (2 * D);
+  float x[CHS];
 #pragma unroll
-    for (int u = 0; u < NBT; ++u) {
-      if (pl[u] > 0.0f) {
-        const float mn = fmaxf(m_run, pm[u]);
-        const float co = expf(m_run - mn), w = expf(pm[u] - mn);
-        l_run = fmaf(l_run, co, w * pl[u]);
+  for (int u = 0; u < CHS; ++u) {
+    const int s = sg + SGN * u;
+    x[u] = s < ns ? base[size_t(s) * stride + 2 + e] : 0.0f;
+  }
+  // step 1
+  float mmax = -INFINITY;
+  for (int s = tid; s < ns; s += NT) {
+    const float ms = base[size_t(s) * stride], ls = base[size_t(s) * stride + 1];
+    ws_l[s] = ls > 0.0f ? ms : -INFINITY;
+    ls_l[s] = ls > 0.0f ? ls : 0.0f;
+    mmax = fmaxf(mmax, ws_l[s]);
+  }
 #pragma unroll
-        for (int e = 0; e < EPT / 2; ++e) {
-          acc[2 * e] = fmaf(acc[2 * e], co, w * x[u][e].x);
-          acc[2 * e + 1] = fmaf(acc[2 * e + 1], co, w * x[u][e].y);
-        }
-        m_run = mn;
+  for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, o, kWave));
+  if (lane == 0) red[wave] = mmax;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  float lsum = 0.0f;
+  for (int s = tid; s < ns; s += NT) {
+    const float ms = ws_l[s];
+    const float w = ms > -INFINITY ? expf(ms - M) : 0.0f;
+    lsum = fmaf(w, ls_l[s], lsum);
+    ws_l[s] = w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o, kWave);
+  if (lane == 0) red[wave] = lsum;
+  __syncthreads();
+  float l = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) l += red[w];
+  // step 2
+  float acc = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += SGN * CHS) {
+    if (s0 > 0)
+#pragma unroll
+      for (int u = 0; u < CHS; ++u) {
+        const int s = s0 + sg + SGN * u;
+        x[u] = s < ns ? base[size_t(s) * stride + 2 + e] : 0.0f;
       }
+#pragma unroll
+    for (int u = 0; u < CHS; ++u) {
+      const int s = s0 + sg + SGN * u;
+      const float w = s < ns ? ws_l[s] : 0.0f;
+      acc = w > 0.0f ? fmaf(w, x[u], acc) : acc;  // a split without tokens has stale (A, B)
     }
   }
-  if (eg == 0) {
-    ms_s[sg] = m_run;
-    ls_s[sg] = l_run;
-  }
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) part_s[sg][eg * EPT + e] = acc[e];
+  accg[sg][e] = e < D ? acc : a.kappa * acc;
   __syncthreads();
-  float M = -INFINITY;
+  // step 3
+  float v[RPT];
 #pragma unroll
-  for (int g = 0; g < 16; ++g) M = fmaxf(M, ls_s[g] > 0.0f ? ms_s[g] : -INFINITY);
-  float wg[16], l = 0.0f;
+  for (int i = 0; i < RPT; ++i) {
+    v[i] = 0.0f;
 #pragma unroll
-  for (int g = 0; g < 16; ++g) {
-    wg[g] = ls_s[g] > 0.0f ? expf(ms_s[g] - M) : 0.0f;
-    l = fmaf(wg[g], ls_s[g], l);
+    for (int g = 0; g < SGN; ++g) v[i] += accg[g][kq + 8 * i];
   }
-  for (int e = tid; e < 2 * D; e += 256) {
-    float v = 0.0f;
-#pragma unroll
-    for (int g = 0; g < 16; ++g) v = fmaf(wg[g], part_s[g][e], v);
-    AB[e] = v;
-  }
-  __syncthreads();
-  // projection: thread (kg, jg) sums rows k in [kg * KPER, (kg + 1) * KPER) for
-  // output columns 4 jg .. 4 jg + 3, KCH rows' loads at a time
-  {
-    float4 x = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 1
-    for (int k0 = 0; k0 < KPER; k0 += KCH) {
-      float4 r[KCH], sp[KCH];
-#pragma unroll
-      for (int kk = 0; kk < KCH; ++kk) {
-        const int k = kg * KPER + k0 + kk;
-        r[kk] = k0 == 0 ? r0[kk] : *reinterpret_cast<const float4 *>(a.rot + size_t(k) * D + 4 * jg);
-        sp[kk] = k0 == 0 ? sp0[kk]
-                         : (skv ? *reinterpret_cast<const float4 *>(a.proj + size_t(k) * D + 4 * jg) : float4{0, 0, 0, 0});
-      }
-#pragma unroll
-      for (int kk = 0; kk < KCH; ++kk) {
-        const int k = kg * KPER + k0 + kk;
-        const float av = AB[k], bv = a.kappa * AB[D + k];
-        x.x = fmaf(sp[kk].x, bv, fmaf(r[kk].x, av, x.x));
-        x.y = fmaf(sp[kk].y, bv, fmaf(r[kk].y, av, x.y));
-        x.z = fmaf(sp[kk].z, bv, fmaf(r[kk].z, av, x.z));
-        x.w = fmaf(sp[kk].w, bv, fmaf(r[kk].w, av, x.w));
-      }
+  for (int cg = 0; cg < CPB; ++cg) {
+    const int col0 = 64 * (CPB * cs + cg);
+    if (cg > 0) {
+      load_rows(col0 + jj);
+      __syncthreads();  // prj of the previous group has been read
     }
-    *reinterpret_cast<float4 *>(&prj[kg][4 * jg]) = x;
-  }
-  __syncthreads();
-  for (int j = tid; j < D; j += 256) {
-    float o = 0.0f;
+    float pj = 0.0f;
 #pragma unroll
-    for (int g = 0; g < KG; ++g) o += prj[g][j];
-    a.out[bh * D + j] = l > 0.0f ? o / l : 0.0f;
+    for (int i = 0; i < RPT; ++i) pj = fmaf(mrow[i], v[i], pj);
+    prj[kq][jj] = pj;
+    __syncthreads();
+    if (tid < 64) {
+      float o = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) o += prj[g][tid];
+      a.out[size_t(bh) * D + col0 + tid] = l > 0.0f ? o / l : 0.0f;
+    }
   }
 }
 
 template <int D, int RB, int BQK>
 int launch_partial_bv(int bqv, const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hkv, a.batch);
-  if (a.split_tokens > kMaxT * 256) return 1;
+  if (a.split_tokens > kMaxT * 256 || a.n_split > kMaxSplits) return 1;
   switch (bqv) {
     case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1>), grid, dim3(256), 0, s, a); return 0;
     case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2>), grid, dim3(256), 0, s, a); return 0;
@@ -880,7 +879,8 @@ int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq), dim3(256), 0, s, a);
   int e = rb == 1 ? launch_partial<D, 1>(a, s) : launch_partial<D, 2>(a, s);
   if (e) return e;
-  hipLaunchKernelGGL(decode_merge_fast<D>, dim3(nq), dim3(256), 0, s, a);
+  if (nq >= 128) hipLaunchKernelGGL((decode_merge_fast<D, D / 64>), dim3(nq), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((decode_merge_fast<D, 1>), dim3(nq * (D / 64)), dim3(512), 0, s, a);
   return 0;
 }
 

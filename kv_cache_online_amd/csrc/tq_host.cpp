@@ -134,6 +134,7 @@ DecodePlan decode_plan(const tq_config &cfg, int32_t batch, int32_t max_len) {
   // slots into its first split.
   p.n_split = static_cast<int32_t>((int64_t(max_len) + 63 + st - 1) / st);
   if (p.n_split < 1) p.n_split = 1;
+  if (p.n_split > 2048) p.fast = 0;  // the matrix-core merge keeps one weight per split in LDS
   p.part_stride = 2 + cfg.d + cfg.m;
   const size_t nq = size_t(batch) * cfg.n_q_heads;
   const size_t nkv = size_t(batch) * cfg.n_kv_heads;
