@@ -99,7 +99,7 @@ struct DecodeArgs {
   double walsh_k[4];     // key codebook Walsh coefficients, planes ordered s0, s1, s2, s0 s1 s2
   double walsh_v[4];     // value codebook, same order
   void *qop;             // matrix-core A operands of the queries (fast path)
-  int32_t *qconst;       // [batch][Hq][8]: index / sign correction as (hi, lo), alpha, beta (fp32 bits), 0, 0
+  int32_t *qconst;       // [batch][Hq][8]: at 4 and 5 alpha and beta (fp32 bits) of the score digit sums
   const void *q;         // [batch][Hq][d]
   int32_t dtype;
   int32_t batch, Hkv, Hq, G;
@@ -111,6 +111,7 @@ struct DecodeArgs {
   const float *proj;     // S [m][d]
   const float *rotT;
   const float *projT;
+  const float *stnorm;   // row norms of S~ = S Pi^T [m]
   float *qr;             // [batch][Hq][d]
   float *qs;             // [batch][Hq][m]
   float *part;           // [batch][Hq][n_split][2 + d + m]

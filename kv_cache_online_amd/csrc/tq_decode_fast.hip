@@ -106,140 +106,98 @@ __device__ inline void clip_seq(const DecodeArgs &a, int b, int64_t *start, int6
 }
 
 // ------------------------------------------------------------- query prep ---
-// One block per (sequence, query head): q_rot = Pi q and q_s = S q in fp32
-// (the products carry about 2^-24 relative error, far inside what the scores
-// need), then this head's four rows (one per digit) of every score operand,
-// written as 16-byte lane entries, and the exact correction constants
-// sum_j F_j 2^shift_j.
-// The contraction reads the transposed matrices [Pi^T | S^T] (k rows, 2D
-// columns) so that a wave's loads are contiguous: thread (kg, cg) sums rows
-// k in its k-group for the four columns 4 cg .. 4 cg + 3, its first chunk of
-// loads issued before q arrives; the k-groups are then added in LDS.
+// Block (sequence, query head, slice t) of 2 d / 64: slice t < d / 64 covers
+// coordinates 64 t .. 64 t + 63 of q_rot = Pi q (the Walsh planes' operands),
+// slice t >= d / 64 the same coordinates of q_s = S q (the sign plane's).  It
+// computes its 64 products in fp32 (about 2^-24 relative error, far inside what
+// the scores need) from the transposed matrices, so that a wave's loads are
+// contiguous, and writes this head's four rows (one per digit) of its operand
+// entries.  The fixed-point exponent of a plane must be the same in every
+// slice, so it comes from a bound every slice can compute: |(Pi q)_j| <= ||q||
+// (Pi is orthogonal) and |(S q)_i| <= max_i ||S_i|| ||q|| (the row norms of
+// S~ = S Pi^T, equal to those of S), with 2^-10 to spare for rounding.  The
+// exact corrections sum_j F_j 2^shift_j are summed by the split pass.
 template <int D>
 __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
-  constexpr int C = D / 64;
-  constexpr int NCG = 2 * D / 4, NKG = 256 / NCG, KPER = D / NKG, CH = 32;  // column / k groups
-  __shared__ __attribute__((aligned(16))) float q[D];
-  __shared__ __attribute__((aligned(16))) float part[NKG][2 * D];
-  __shared__ float qr[D], qs[D];
-  __shared__ float wmax[2][4];
-  __shared__ double wsum[2][4];
+  constexpr int C = D / 64, NSL = 2 * D / 64, KPT = D / 4;
+  __shared__ float q[D];
+  __shared__ float part[4][64];
+  __shared__ float vals[64];
+  __shared__ float red[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bh = blockIdx.x, b = bh / a.Hq, hq = bh % a.Hq;
+  const int bh = blockIdx.x / NSL, t = blockIdx.x % NSL;
+  const int b = bh / a.Hq, hq = bh % a.Hq;
   const int kvh = hq / a.G, hl = hq % a.G, rb = hl >> 2, row0 = (hl & 3) * 4;
   const int RB = a.G / 4;
-  const int cg = tid % NCG, kg = tid / NCG;
-  const bool isr = 4 * cg < D;
-  const float *mt = isr ? a.rotT + 4 * cg : a.projT + (4 * cg - D);  // column block of row 0
-  const int k0 = kg * KPER;
-  float4 m[CH];
+  const bool sgn = t >= D / 64;
+  if (sgn && !a.k.sketch) return;  // no sign plane
+  const int c0 = (sgn ? t - D / 64 : t) * 64;
+  // column c0 + lane of Pi^T or S^T, rows wave KPT .. wave KPT + KPT - 1
+  const float *mt = (sgn ? a.projT : a.rotT) + c0 + lane + size_t(wave) * KPT * D;
+  float m[KPT];
 #pragma unroll
-  for (int k = 0; k < CH; ++k) m[k] = *reinterpret_cast<const float4 *>(mt + size_t(k0 + k) * D);
-  for (int j = tid; j < D; j += 256) q[j] = load_q(a.q, a.dtype, size_t(bh) * D + j);
-  __syncthreads();
-  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 1
-  for (int kc = 0; kc < KPER; kc += CH) {
-    if (kc > 0)
-#pragma unroll
-      for (int k = 0; k < CH; ++k) m[k] = *reinterpret_cast<const float4 *>(mt + size_t(k0 + kc + k) * D);
-#pragma unroll
-    for (int k = 0; k < CH; k += 4) {
-      const float4 x = *reinterpret_cast<const float4 *>(&q[k0 + kc + k]);
-      const float xv[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc.x = fmaf(m[k + u].x, xv[u], acc.x);
-        acc.y = fmaf(m[k + u].y, xv[u], acc.y);
-        acc.z = fmaf(m[k + u].z, xv[u], acc.z);
-        acc.w = fmaf(m[k + u].w, xv[u], acc.w);
-      }
-    }
-  }
-  *reinterpret_cast<float4 *>(&part[kg][4 * cg]) = acc;
-  __syncthreads();
-  float mr = 0.0f, ms = 0.0f;
-  for (int c = tid; c < 2 * D; c += 256) {
-    float v = 0.0f;
-#pragma unroll
-    for (int g = 0; g < NKG; ++g) v += part[g][c];
-    if (c < D) {
-      qr[c] = v;
-      mr = fmaxf(mr, fabsf(v));
-    } else {
-      qs[c - D] = v;
-      ms = fmaxf(ms, fabsf(v));
-    }
+  for (int i = 0; i < KPT; ++i) m[i] = mt[size_t(i) * D];
+  float ss = 0.0f, smax = 0.0f;
+  for (int j = tid; j < D; j += 256) {
+    const float v = load_q(a.q, a.dtype, size_t(bh) * D + j);
+    q[j] = v;
+    ss = fmaf(v, v, ss);
+    if (sgn) smax = fmaxf(smax, a.stnorm[j]);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    mr = fmaxf(mr, __shfl_xor(mr, o, kWave));
-    ms = fmaxf(ms, __shfl_xor(ms, o, kWave));
+    ss += __shfl_xor(ss, o, kWave);
+    smax = fmaxf(smax, __shfl_xor(smax, o, kWave));
   }
   if (lane == 0) {
-    wmax[0][wave] = mr;
-    wmax[1][wave] = ms;
+    red[0][wave] = ss;
+    red[1][wave] = smax;
   }
   __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) acc = fmaf(m[i], q[wave * KPT + i], acc);
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (tid < 64) vals[tid] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+  const float nq = sqrtf((red[0][0] + red[0][1]) + (red[0][2] + red[0][3]));
   const int npk = n_walsh(a.k.bq);
   double amax = 0.0;
   for (int p = 0; p < npk; ++p) amax = fmax(amax, fabs(a.walsh_k[p]));
-  const float maxr = fmaxf(fmaxf(wmax[0][0], wmax[0][1]), fmaxf(wmax[0][2], wmax[0][3]));
-  const float maxs = fmaxf(fmaxf(wmax[1][0], wmax[1][1]), fmaxf(wmax[1][2], wmax[1][3]));
-  const int Ei = fix_exp(amax * maxr), Es = fix_exp(maxs);
-  uint4 *op = reinterpret_cast<uint4 *>(static_cast<unsigned char *>(a.qop) +
-                                        (size_t(b * a.Hkv + kvh) * RB + rb) * 5 * C * kWave * 16);
-  const int nplane = npk + a.k.sketch;
-  double ki = 0.0, ks = 0.0;
+  const double scale =
+      sgn ? double(fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]))) : amax;
+  const int E = fix_exp(scale * double(nq) * (1.0 + 0x1p-10));
+  __syncthreads();
   // entry = (plane, chunk c, lane group g, digit l): 16 bytes for VGPR s, byte i.
   // Lane group g owns plane words g, g + 4, ...; chunk c takes word g + 4 (c >> 1)
   // and its nibble c & 1: byte i of VGPR s is coordinate 32 (g + 4 (c >> 1)) + 8 i + s + 4 (c & 1).
-  for (int e = tid; e < nplane * C * 16; e += 256) {
-    const int l = e & 3, g = (e >> 2) & 3, c = (e >> 4) % C, pidx = (e >> 4) / C;
-    const bool sign = pidx == npk;
-    const float wk = sign ? 1.0f : static_cast<float>(a.walsh_k[pidx]);
-    const int E = sign ? Es : Ei;
+  // The slice holds words c0 / 32 and c0 / 32 + 1, both nibbles: 4 (g, c) pairs.
+  uint4 *op = reinterpret_cast<uint4 *>(static_cast<unsigned char *>(a.qop) +
+                                        (size_t(b * a.Hkv + kvh) * RB + rb) * 5 * C * kWave * 16);
+  const int nplane = sgn ? 1 : npk;
+  if (tid < nplane * 16) {
+    const int l = tid & 3, hw = (tid >> 2) & 3, pidx = tid >> 4;
+    const int w = c0 / 32 + (hw >> 1), h = hw & 1, g = w & 3, c = 2 * (w >> 2) + h;
+    const float wk = sgn ? 1.0f : static_cast<float>(a.walsh_k[pidx]);
     uint32_t wv[4] = {0u, 0u, 0u, 0u};
-    int64_t ksum = 0;
 #pragma unroll
     for (int sv = 0; sv < 4; ++sv)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = 32 * (g + 4 * (c >> 1)) + 8 * i + sv + 4 * (c & 1);
-        const float v = sign ? qs[j] : wk * qr[j];
-        const int32_t F = static_cast<int32_t>(rintf(ldexpf(v, E - sv)));
-        ksum += int64_t(F) * (int64_t(1) << sv);
-        const uint32_t dg = digits(F);
-        wv[sv] |= ((dg >> (8 * l)) & 0xFFu) << (8 * i);
+        const int j = 32 * w + 8 * i + sv + 4 * h;
+        const int32_t F = static_cast<int32_t>(rintf(ldexpf(wk * vals[j - c0], E - sv)));
+        wv[sv] |= ((digits(F) >> (8 * l)) & 0xFFu) << (8 * i);
       }
-    if (l == 0) {
-      if (sign) ks += double(ksum);
-      else ki += double(ksum);
-    }
-    const int slot = sign ? kSigPlane : pidx;
+    const int slot = sgn ? kSigPlane : pidx;
     op[(size_t(slot) * C + c) * kWave + 16 * g + row0 + l] = uint4{wv[0], wv[1], wv[2], wv[3]};
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    ki += __shfl_xor(ki, o, kWave);
-    ks += __shfl_xor(ks, o, kWave);
-  }
-  if (lane == 0) {
-    wsum[0][wave] = ki;
-    wsum[1][wave] = ks;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    // the corrections are integers below 2^53, split as 2^17 hi + lo, 0 <= lo < 2^17
+  if (tid == 0 && (t == 0 || t == D / 64)) {
+    // alpha (Walsh planes) or beta (sign plane, 0 without one): the scale of the digit sums
     const double base = double(a.sm_scale) * 1.4426950408889634;  // log2(e): scores in base 2
-    const int64_t ki = static_cast<int64_t>((wsum[0][0] + wsum[0][1]) + (wsum[0][2] + wsum[0][3]));
-    const int64_t ks = static_cast<int64_t>((wsum[1][0] + wsum[1][1]) + (wsum[1][2] + wsum[1][3]));
     int32_t *qc = a.qconst + size_t(bh) * 8;
-    *reinterpret_cast<int4 *>(qc) = make_int4(static_cast<int32_t>(ki >> 17), static_cast<int32_t>(ki & 0x1FFFF),
-                                              static_cast<int32_t>(ks >> 17), static_cast<int32_t>(ks & 0x1FFFF));
-    *reinterpret_cast<int4 *>(qc + 4) =
-        make_int4(__float_as_int(static_cast<float>(ldexp(base, -Ei))),
-                  a.k.sketch ? __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), -Es))) : 0, 0, 0);
+    if (sgn) qc[5] = __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), -E)));
+    else qc[4] = __float_as_int(static_cast<float>(ldexp(base, -E)));
+    if (!sgn && !a.k.sketch) qc[5] = 0;
   }
 }
 
@@ -384,7 +342,6 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   const int ntile = static_cast<int>((hi - abase + 63) >> 6);
   const int vlo = static_cast<int>(lo - abase), vhi = static_cast<int>(hi - abase);  // valid slots
   const uint32_t sh = (grp & 1) ? 4u : 0u;  // value operand: odd nibbles, shift the word right by 4
-  const uint32_t msk[4] = {0x01010101u, 0x02020202u, 0x04040404u, 0x08080808u};
   const int64_t kcap = a.k.cap, vcap = a.v.cap, vblocks = vcap >> 5;
   const bool skk = a.k.sketch != 0, skv = a.v.sketch != 0;
   const int kslots = static_cast<int>((kcap - abase) < S ? (kcap - abase) : S);
@@ -441,7 +398,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
 #pragma unroll
   for (int s = 0; s < kSlots - 1; ++s) issue(s);
   v4i qa[RB][PK + 1][C];
-  int4 qk[RB], qf[RB];  // per head: correction hi/lo (index, sign), alpha and beta bits
+  int2 qf[RB];  // per head: alpha and beta (fp32 bits)
   {
     const v4i *qop = static_cast<const v4i *>(a.qop) + size_t(b * a.Hkv + h) * RB * 5 * C * kWave;
 #pragma unroll
@@ -453,9 +410,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
         for (int c = 0; c < C; ++c)
           qa[rb][p][c] = (p < PK || skk) ? qop[((size_t(rb) * 5 + slot) * C + c) * kWave + lane] : v4i{0, 0, 0, 0};
       }
-      const int4 *qc = reinterpret_cast<const int4 *>(a.qconst + size_t(bh0 + rb * 4 + grp) * 8);
-      qk[rb] = qc[0];
-      qf[rb] = qc[1];
+      qf[rb] = *reinterpret_cast<const int2 *>(a.qconst + size_t(bh0 + rb * 4 + grp) * 8 + 4);
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -464,8 +419,31 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < C; ++c)
           asm volatile("" ::"v"(qa[rb][p][c].x), "v"(qa[rb][p][c].y), "v"(qa[rb][p][c].z), "v"(qa[rb][p][c].w));
-      asm volatile("" ::"v"(qk[rb].x), "v"(qk[rb].y), "v"(qk[rb].z), "v"(qk[rb].w), "v"(qf[rb].x), "v"(qf[rb].y));
+      asm volatile("" ::"v"(qf[rb].x), "v"(qf[rb].y));
     }
+  }
+  const uint32_t msk[4] = {0x01010101u, 0x02020202u, 0x04040404u, 0x08080808u};
+  const v4i ones = {static_cast<int>(msk[0]), static_cast<int>(msk[1]), static_cast<int>(msk[2]),
+                    static_cast<int>(msk[3])};
+  // The +-1 corrections k = sum_j F_j 2^shift_j of the index planes (summed) and
+  // of the sign plane: the query operands against all-ones bit planes, exact
+  // digit sums, split as k = 2^17 KH + KL with 0 <= KL < 2^17.
+  int32_t khi[RB], kli[RB], khs[RB], kls[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    v4i ci = {0, 0, 0, 0}, cs = {0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+#pragma unroll
+      for (int p = 0; p < PK; ++p) ci = mfma(qa[rb][p][c], ones, ci);
+      cs = mfma(qa[rb][PK][c], ones, cs);
+    }
+    const int64_t ki = int64_t(ci.x) + (int64_t(ci.y) << 8) + (int64_t(ci.z) << 16) + (int64_t(ci.w) << 24);
+    const int64_t ks = int64_t(cs.x) + (int64_t(cs.y) << 8) + (int64_t(cs.z) << 16) + (int64_t(cs.w) << 24);
+    khi[rb] = static_cast<int32_t>(ki >> 17);
+    kli[rb] = static_cast<int32_t>(ki & 0x1FFFF);
+    khs[rb] = static_cast<int32_t>(ks >> 17);
+    kls[rb] = static_cast<int32_t>(ks & 0x1FFFF);
   }
 
   // ---- phase 1: scores of this wave's key tiles, kept in registers ----
@@ -516,8 +494,8 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
         vrhomax = fmaxf(vrhomax, valid ? f16v(vsc >> 16) : 0.0f);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          const float ri = score_sum(acc_i[rb], qk[rb].x, qk[rb].y);
-          const float rs = score_sum(acc_s[rb], qk[rb].z, qk[rb].w);
+          const float ri = score_sum(acc_i[rb], khi[rb], kli[rb]);
+          const float rs = score_sum(acc_s[rb], khs[rb], kls[rb]);
           float sv = fmaf(knu * __int_as_float(qf[rb].x), ri, (krho * __int_as_float(qf[rb].y)) * rs);
           sv = valid ? sv : -INFINITY;
           sreg[kt][nb][rb] = sv;
@@ -566,8 +544,6 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
       for (int rb = 0; rb < RB; ++rb) av[p][nb][rb] = v4i{0, 0, 0, 0};
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) ak[0][rb] = ak[1][rb] = v4i{0, 0, 0, 0};
-  const v4i ones = {static_cast<int>(msk[0]), static_cast<int>(msk[1]), static_cast<int>(msk[2]),
-                    static_cast<int>(msk[3])};
   float lloc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) lloc[rb] = 0.0f;
@@ -876,7 +852,7 @@ int launch_partial(const DecodeArgs &a, hipStream_t s) {
 template <int D>
 int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
   const unsigned nq = static_cast<unsigned>(a.batch * a.Hq);
-  hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
   int e = rb == 1 ? launch_partial<D, 1>(a, s) : launch_partial<D, 2>(a, s);
   if (e) return e;
   if (nq >= 128) hipLaunchKernelGGL((decode_merge_fast<D, D / 64>), dim3(nq), dim3(512), 0, s, a);

@@ -482,6 +482,7 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
   a.proj = cfg->proj;
   a.rotT = reinterpret_cast<const float *>(prep + L.rotT);
   a.projT = reinterpret_cast<const float *>(prep + L.projT);
+  a.stnorm = reinterpret_cast<const float *>(prep + L.stnorm);
   a.qr = reinterpret_cast<float *>(ws + p.off_qr);
   a.qs = reinterpret_cast<float *>(ws + p.off_qs);
   a.part = reinterpret_cast<float *>(ws + p.off_part);
