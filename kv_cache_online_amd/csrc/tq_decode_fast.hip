@@ -214,8 +214,8 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
 // block and grp the token group of the contraction.
 //
 // Data movement: every wave streams its own chunks through a private ring of
-// kSlots LDS slots with buffer loads that write LDS directly (16 bytes per lane,
-// no VGPRs), kSlots - 1 chunks ahead of the one it computes on.  A wave's
+// LDS slots with buffer loads that write LDS directly (16 bytes per lane, no
+// VGPRs), one chunk fewer than the slots ahead of the one it computes on.  A wave's
 // stream is its key tiles (tiles wave, wave + 4, ...: planes, signs, key and
 // value scales, each a contiguous run of the token-major cache), then one value
 // chunk per round (its quarter of the coordinates of the round's 8 value blocks,
@@ -224,7 +224,6 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
 //
 // Scores never leave registers: the lane that scores (head, token) in phase 1
 // is the lane that turns it into a weight in phase 2.
-constexpr int kSlots = 3;  // ring slots per wave
 constexpr int kMaxT = 4;   // key tiles per wave and split: split <= 1024 slots
 
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
@@ -300,7 +299,12 @@ struct SplitShape {
   static constexpr int SLOT = K_BYTES > V_BYTES ? K_BYTES : V_BYTES;
   static constexpr int NI_K = (BQK + 1) * NW + 2, NI_V = (BQV + 1) * NW;  // loads per chunk
   static constexpr int NI_MIN = NI_K < NI_V ? NI_K : NI_V;
-  static constexpr int AWP = RB == 1 ? 2 : 1;  // value operand buffers (round parity)
+  // Ring slots per wave and value operand buffers (round parity).  With two
+  // head blocks the split pass is bound by its ALU work, so it takes the smaller
+  // LDS footprint that fits three work-groups per CU; with one it is bound by
+  // memory latency and keeps two chunks in flight per wave.
+  static constexpr int SLOTS = RB == 1 ? 3 : 2;
+  static constexpr int AWP = RB == 1 ? 2 : 1;
 };
 
 template <int D, int RB, int BQK, int BQV>
@@ -308,6 +312,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   using P = SplitShape<D, RB, BQK, BQV>;
   constexpr int C = P::C, W = P::W, NB = P::NB, NW = P::NW, G = P::G, PK = P::PK, PV = P::PV;
   constexpr int KREC = P::KREC, KSREC = P::KSREC, VREC = P::VREC, VSREC = P::VSREC, AWP = P::AWP;
+  constexpr int kSlots = P::SLOTS;
   __shared__ __attribute__((aligned(16))) unsigned char ring[4][kSlots][P::SLOT];
   // value A operands of a round: [round parity][part][tile][kgroup][rb][row][byte]
   __shared__ __attribute__((aligned(16))) unsigned char aw[AWP][2][4][4][RB][16][16];
