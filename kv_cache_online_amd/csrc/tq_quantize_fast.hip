@@ -54,6 +54,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int NPX, int BQ>
 struct QSmem {
+  __align__(16) uint16_t plo[NPX == 1 ? QD : 1][XS];  // lo piece of Pi (bf16 bits; bf16 input only)
   __align__(16) uint16_t xs[NPX][QT][XS];    // input pieces (bf16 bits)
   __align__(16) uint16_t rh[QT][XS];         // residual, hi piece
   __align__(16) uint16_t rm[QT][XS];         // residual, mid piece
@@ -192,9 +193,20 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
   const bool sk = a.t.sketch != 0;
 
   // Row operands: rows cw + 16 rb + li of Pi and S~, 8 consecutive columns per lane group.
-  bf16x8 pia[3][2][4], sta[2][2][4];
+  // The wave's rows of Pi and S~ in registers.  For bf16 input the lo piece of Pi
+  // (whose products are 2^-16 of the total) is read from LDS instead, which frees
+  // the registers that let a row block's compares overlap the next block's
+  // products; fp32 input needs the LDS for its own three pieces.
+  constexpr int NPI = F32 ? 3 : 2;
+  bf16x8 pia[NPI][2][4], sta[2][2][4];
+  if (!F32)
+    for (int i = t; i < QD * QD / 8; i += QN) {
+      const int r = i / (QD / 8), c8 = i % (QD / 8);
+      *reinterpret_cast<uint4 *>(&sm.plo[r][8 * c8]) =
+          *reinterpret_cast<const uint4 *>(a.rot_hml + (size_t(2) * QD + r) * QD + 8 * c8);
+    }
 #pragma unroll
-  for (int p = 0; p < 3; ++p)
+  for (int p = 0; p < NPI; ++p)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -318,44 +330,43 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
     __syncthreads();
 
     // ---------------------------------------------------------------- B --
+    // Row block by row block: the compares of block 0 need only its own
+    // products, so they can issue while block 1's products run on the matrix pipe.
     {
-      f32x4 acc[2][2];
+      PlaneBits pb[BQ];
+      float rr[2] = {0.0f, 0.0f};
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) acc[rb][g2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kc = 0; kc < 4; ++kc) {
+          bf16x8 xb[2][NPX];
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        bf16x8 xb[2][NPX];
+          for (int g2 = 0; g2 < 2; ++g2)
 #pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2)
+            for (int px = 0; px < NPX; ++px)
+              xb[g2][px] = *reinterpret_cast<const bf16x8 *>(&sm.xs[px][16 * g2 + li][32 * kc + 8 * lg]);
+          const bf16x8 plo = F32 ? pia[NPI - 1][rb][kc]
+                                 : *reinterpret_cast<const bf16x8 *>(&sm.plo[F32 ? 0 : cw + 16 * rb + li][32 * kc + 8 * lg]);
 #pragma unroll
           for (int px = 0; px < NPX; ++px)
-            xb[g2][px] = *reinterpret_cast<const bf16x8 *>(&sm.xs[px][16 * g2 + li][32 * kc + 8 * lg]);
 #pragma unroll
-        for (int px = 0; px < NPX; ++px)
-#pragma unroll
-          for (int pp = 0; pp < (F32 ? 3 - px : 3); ++pp)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int pp = 0; pp < (F32 ? 3 - px : 3); ++pp)
 #pragma unroll
               for (int g2 = 0; g2 < 2; ++g2)
-                acc[rb][g2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pia[pp][rb][kc], xb[g2][px], acc[rb][g2], 0, 0, 0);
-      }
-      // acc[rb][g2] lane (li, lg) register r: coordinate cw + 16 rb + 4 lg + r of vector 16 g2 + li
-      PlaneBits pb[BQ];
+                acc[g2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp < 2 ? pia[pp][rb][kc] : plo, xb[g2][px], acc[g2],
+                                                                  0, 0, 0);
+        }
+        // acc[g2] lane (li, lg) register r: coordinate cw + 16 rb + 4 lg + r of vector 16 g2 + li
 #pragma unroll
-      for (int g2 = 0; g2 < 2; ++g2) {
-        const int vv = 16 * g2 + li;
-        const f32x4 th = *reinterpret_cast<const f32x4 *>(&sm.vth[vv][0]);
-        const f32x4 cs = *reinterpret_cast<const f32x4 *>(&sm.vth[vv][4]);
-        float rr = 0.0f;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int vv = 16 * g2 + li;
+          const f32x4 th = *reinterpret_cast<const f32x4 *>(&sm.vth[vv][0]);
+          const f32x4 cs = *reinterpret_cast<const f32x4 *>(&sm.vth[vv][4]);
           float rho[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float z = acc[rb][g2][r];
+            const float z = acc[g2][r];
             const float az = fabsf(z);
             const bool pos = z >= 0.0f;
             float val = cs[0];
@@ -367,7 +378,7 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
               cm[k] = __ballot(c);
             }
             rho[r] = z - (pos ? val : -val);
-            rr = fmaf(rho[r], rho[r], rr);
+            rr[g2] = fmaf(rho[r], rho[r], rr[g2]);
             const uint64_t pm = __ballot(pos);
             // cell = L/2 + m above zero, L/2 - 1 - m below, with m the number of
             // positive boundaries <= |u|; bit q < BQ-1 of m is the parity of the
@@ -385,22 +396,24 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
               pb[q].put(bits, rb, g2, r);
             }
           }
-          if (sk) {
-            const uint32_t h01 = cvt_pk_bf16(rho[0], rho[1]), h23 = cvt_pk_bf16(rho[2], rho[3]);
-            const uint32_t m01 =
-                cvt_pk_bf16(rho[0] - __uint_as_float(h01 << 16), rho[1] - __uint_as_float(h01 & 0xFFFF0000u));
-            const uint32_t m23 =
-                cvt_pk_bf16(rho[2] - __uint_as_float(h23 << 16), rho[3] - __uint_as_float(h23 & 0xFFFF0000u));
-            const int c = cw + 16 * rb + 4 * lg;
-            *reinterpret_cast<uint2 *>(&sm.rh[vv][c]) = make_uint2(h01, h23);
-            *reinterpret_cast<uint2 *>(&sm.rm[vv][c]) = make_uint2(m01, m23);
-          }
+          // residual pieces for the sketch (written whether or not it runs: no branch
+          // here, so the two row blocks stay one straight run of code)
+          const uint32_t h01 = cvt_pk_bf16(rho[0], rho[1]), h23 = cvt_pk_bf16(rho[2], rho[3]);
+          const uint32_t m01 =
+              cvt_pk_bf16(rho[0] - __uint_as_float(h01 << 16), rho[1] - __uint_as_float(h01 & 0xFFFF0000u));
+          const uint32_t m23 =
+              cvt_pk_bf16(rho[2] - __uint_as_float(h23 << 16), rho[3] - __uint_as_float(h23 & 0xFFFF0000u));
+          const int c = cw + 16 * rb + 4 * lg;
+          *reinterpret_cast<uint2 *>(&sm.rh[vv][c]) = make_uint2(h01, h23);
+          *reinterpret_cast<uint2 *>(&sm.rm[vv][c]) = make_uint2(m01, m23);
         }
-        if (sk) {
-          rr += __shfl_xor(rr, 16, kWave);
-          rr += __shfl_xor(rr, 32, kWave);
-          if (lg == 0) sm.rr[w][vv] = rr;
-        }
+      }
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        float v = rr[g2];
+        v += __shfl_xor(v, 16, kWave);
+        v += __shfl_xor(v, 32, kWave);
+        if (lg == 0) sm.rr[w][16 * g2 + li] = v;
       }
 #pragma unroll
       for (int q = 0; q < BQ; ++q) pb[q].store(sm.wst[q], lane, cw);
