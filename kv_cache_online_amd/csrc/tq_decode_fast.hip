@@ -201,6 +201,101 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   }
 }
 
+// Query prep for many query heads: block (group of 8 heads, slice t), the same
+// work as decode_qprep_fast for each head, with the slice of the transposed
+// matrix read once for the group.
+template <int D>
+__global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq) {
+  constexpr int C = D / 64, NSL = 2 * D / 64, KPT = D / 4, HG = 8;
+  __shared__ float q[HG][D];
+  __shared__ float part[HG][4][64];
+  __shared__ float vals[HG][64];
+  __shared__ float qn[HG];
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = blockIdx.x / NSL, t = blockIdx.x % NSL;
+  const bool sgn = t >= D / 64;
+  if (sgn && !a.k.sketch) return;  // no sign plane
+  const int c0 = (sgn ? t - D / 64 : t) * 64;
+  const float *mt = (sgn ? a.projT : a.rotT) + c0 + lane + size_t(wave) * KPT * D;
+  float m[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) m[i] = mt[size_t(i) * D];
+  float smax = 0.0f;
+  if (sgn)
+    for (int j = tid; j < D; j += 256) smax = fmaxf(smax, a.stnorm[j]);
+  for (int i = tid; i < HG * D; i += 256) {
+    const int h = i / D, j = i % D, bh = grp * HG + h;
+    q[h][j] = bh < nq ? load_q(a.q, a.dtype, size_t(bh) * D + j) : 0.0f;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) smax = fmaxf(smax, __shfl_xor(smax, o, kWave));
+  if (lane == 0) red[wave] = smax;
+  __syncthreads();
+  // ||q|| of heads HG / 4 wave ..
+#pragma unroll
+  for (int u = 0; u < HG / 4; ++u) {
+    const int h = HG / 4 * wave + u;
+    float ss = 0.0f;
+    for (int j = lane; j < D; j += 64) ss = fmaf(q[h][j], q[h][j], ss);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+    if (lane == 0) qn[h] = sqrtf(ss);
+  }
+#pragma unroll
+  for (int h = 0; h < HG; ++h) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) acc = fmaf(m[i], q[h][wave * KPT + i], acc);
+    part[h][wave][lane] = acc;
+  }
+  __syncthreads();
+  for (int i = tid; i < HG * 64; i += 256) {
+    const int h = i >> 6, c = i & 63;
+    vals[h][c] = (part[h][0][c] + part[h][1][c]) + (part[h][2][c] + part[h][3][c]);
+  }
+  const int npk = n_walsh(a.k.bq);
+  double amax = 0.0;
+  for (int p = 0; p < npk; ++p) amax = fmax(amax, fabs(a.walsh_k[p]));
+  const double scale = sgn ? double(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))) : amax;
+  __syncthreads();
+  const int nplane = sgn ? 1 : npk;
+  for (int e = tid; e < HG * nplane * 16; e += 256) {
+    const int h = e / (nplane * 16), r = e % (nplane * 16), bh = grp * HG + h;
+    if (bh >= nq) continue;
+    const int E = fix_exp(scale * double(qn[h]) * (1.0 + 0x1p-10));
+    const int b = bh / a.Hq, hq = bh % a.Hq;
+    const int kvh = hq / a.G, hl = hq % a.G, rb = hl >> 2, row0 = (hl & 3) * 4, RB = a.G / 4;
+    uint4 *op = reinterpret_cast<uint4 *>(static_cast<unsigned char *>(a.qop) +
+                                          (size_t(b * a.Hkv + kvh) * RB + rb) * 5 * C * kWave * 16);
+    const int l = r & 3, hw = (r >> 2) & 3, pidx = r >> 4;
+    const int w = c0 / 32 + (hw >> 1), hh = hw & 1, g = w & 3, c = 2 * (w >> 2) + hh;
+    const float wk = sgn ? 1.0f : static_cast<float>(a.walsh_k[pidx]);
+    uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int sv = 0; sv < 4; ++sv)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 32 * w + 8 * i + sv + 4 * hh;
+        const int32_t F = static_cast<int32_t>(rintf(ldexpf(wk * vals[h][j - c0], E - sv)));
+        wv[sv] |= ((digits(F) >> (8 * l)) & 0xFFu) << (8 * i);
+      }
+    const int slot = sgn ? kSigPlane : pidx;
+    op[(size_t(slot) * C + c) * kWave + 16 * g + row0 + l] = uint4{wv[0], wv[1], wv[2], wv[3]};
+  }
+  if ((t == 0 || t == D / 64) && tid < HG) {
+    const int bh = grp * HG + tid;
+    if (bh < nq) {
+      const int E = fix_exp(scale * double(qn[tid]) * (1.0 + 0x1p-10));
+      const double base = double(a.sm_scale) * 1.4426950408889634;  // log2(e): scores in base 2
+      int32_t *qc = a.qconst + size_t(bh) * 8;
+      if (sgn) qc[5] = __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), -E)));
+      else qc[4] = __float_as_int(static_cast<float>(ldexp(base, -E)));
+      if (!sgn && !a.k.sketch) qc[5] = 0;
+    }
+  }
+}
+
 // ------------------------------------------------------------ split pass ---
 // One 256-thread block per (split, kv head, sequence); a split holds at most
 // kMaxT * 256 slots.  BQK / BQV: index bits of keys / values (compile time: the
@@ -832,6 +927,113 @@ __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
   }
 }
 
+// Merge for many query heads: block = group of 8 heads, all d outputs.  The
+// per-head blocks above read the whole projection matrix once per head; here
+// one wave merges one head's splits (lane e holds elements e EPT .. e EPT + EPT - 1
+// of (A, B), a running maximum over chunks of CHS splits whose loads are issued
+// together), and the block then applies [Pi ; S], 64 columns at a time, to all
+// eight heads, reading it once per group.
+template <int D>
+__global__ __launch_bounds__(512) void decode_merge_grouped(DecodeArgs a, int nq) {
+  constexpr int HG = 8, EPT = 2 * D / 64, CHS = D == 128 ? 24 : 4, RPT = 2 * D / 8;
+  __shared__ __attribute__((aligned(16))) float ab[HG][2 * D];
+  __shared__ float lg[HG];
+  __shared__ float prj[HG][8][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = blockIdx.x;
+  const int stride = 2 + 2 * D, ns = a.n_split;
+  // the projection's first matrix column group, rows kq + 8 i of [Pi ; S], issued first
+  const int jj = lane, kq = wave;
+  float mrow[RPT];
+  auto load_rows = [&](int col) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int k = kq + 8 * i;
+      mrow[i] = k < D ? a.rot[size_t(k) * D + col] : a.proj[size_t(k - D) * D + col];
+    }
+  };
+  load_rows(jj);
+  // one head per wave
+  const int bh = grp * HG + wave;
+  if (bh < nq) {
+    const float *base = a.part + size_t(bh) * ns * stride;
+    float m_run = -INFINITY, l_run = 0.0f, acc[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) acc[e] = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += CHS) {
+      float pm[CHS], pl[CHS], x[CHS][EPT];
+#pragma unroll
+      for (int u = 0; u < CHS; ++u) {
+        const int s = s0 + u;
+        pm[u] = -INFINITY;
+        pl[u] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) x[u][e] = 0.0f;
+        if (s < ns) {
+          const float *p = base + size_t(s) * stride;
+          pm[u] = p[0];
+          pl[u] = p[1];
+          // element 2 + e sits 8 bytes past a 16-byte boundary: float2 pairs
+#pragma unroll
+          for (int e = 0; e < EPT; e += 2) {
+            const float2 v2 = *reinterpret_cast<const float2 *>(p + 2 + lane * EPT + e);
+            x[u][e] = v2.x;
+            x[u][e + 1] = v2.y;
+          }
+        }
+      }
+      float mc = m_run;
+#pragma unroll
+      for (int u = 0; u < CHS; ++u) mc = pl[u] > 0.0f ? fmaxf(mc, pm[u]) : mc;
+      if (mc > -INFINITY) {
+        const float co = m_run > -INFINITY ? expf(m_run - mc) : 0.0f;
+        l_run *= co;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) acc[e] *= co;
+#pragma unroll
+        for (int u = 0; u < CHS; ++u) {
+          // a split without tokens has stale (A, B)
+          const float w = pl[u] > 0.0f ? expf(pm[u] - mc) : 0.0f;
+          l_run = fmaf(w, pl[u], l_run);
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) acc[e] = w > 0.0f ? fmaf(w, x[u][e], acc[e]) : acc[e];
+        }
+        m_run = mc;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int el = lane * EPT + e;
+      ab[wave][el] = el < D ? acc[e] : a.kappa * acc[e];
+    }
+    if (lane == 0) lg[wave] = l_run;
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int cs = 0; cs < D / 64; ++cs) {
+    if (cs > 0) {
+      load_rows(64 * cs + jj);
+      __syncthreads();  // prj of the previous column group has been read
+    }
+#pragma unroll 1
+    for (int h = 0; h < HG; ++h) {
+      float pj = 0.0f;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) pj = fmaf(mrow[i], ab[h][kq + 8 * i], pj);
+      prj[h][kq][jj] = pj;
+    }
+    __syncthreads();
+    const int h = wave, j = lane, bho = grp * HG + h;
+    if (bho < nq) {
+      float o = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) o += prj[h][g][j];
+      const float l = lg[h];
+      a.out[size_t(bho) * D + 64 * cs + j] = l > 0.0f ? o / l : 0.0f;
+    }
+  }
+}
+
 template <int D, int RB, int BQK>
 int launch_partial_bv(int bqv, const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hkv, a.batch);
@@ -857,10 +1059,15 @@ int launch_partial(const DecodeArgs &a, hipStream_t s) {
 template <int D>
 int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
   const unsigned nq = static_cast<unsigned>(a.batch * a.Hq);
-  hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
+  if (nq >= 512)
+    hipLaunchKernelGGL(decode_qprep_grouped<D>, dim3((nq + 7) / 8 * (2 * D / 64)), dim3(256), 0, s, a, int(nq));
+  else hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
   int e = rb == 1 ? launch_partial<D, 1>(a, s) : launch_partial<D, 2>(a, s);
   if (e) return e;
-  if (nq >= 128) hipLaunchKernelGGL((decode_merge_fast<D, D / 64>), dim3(nq), dim3(512), 0, s, a);
+  // few splits per head: the projection matrix is the larger read, so heads share it
+  if (nq >= 512 && a.n_split <= 64)
+    hipLaunchKernelGGL(decode_merge_grouped<D>, dim3((nq + 7) / 8), dim3(512), 0, s, a, int(nq));
+  else if (nq >= 128) hipLaunchKernelGGL((decode_merge_fast<D, D / 64>), dim3(nq), dim3(512), 0, s, a);
   else hipLaunchKernelGGL((decode_merge_fast<D, 1>), dim3(nq * (D / 64)), dim3(512), 0, s, a);
   return 0;
 }

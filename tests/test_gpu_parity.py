@@ -171,10 +171,11 @@ def test_workload1_full():
     assert run.status() == 0
 
 
-@pytest.mark.parametrize("wid,batch,T", [(2, 1, 1000), (3, 2, 777), (5, 2, 513), (5, 8, 300)])
+@pytest.mark.parametrize("wid,batch,T", [(2, 1, 1000), (3, 2, 777), (5, 2, 513), (5, 8, 300), (5, 32, 100)])
 def test_reduced_workloads(wid, batch, T):
     """(5, 8, 300): 128 query heads of d = 256, where the merge gives each block a
-    whole head (four column groups)."""
+    whole head (four column groups); (5, 32, 100): 512 query heads, where query
+    prep and merge share the matrices across groups of heads."""
     w = W.WORKLOADS[wid]
     run = Run(w, batch=batch, n_tokens=T)
     _log(f"workload {wid} reduced T={T}: quantize")
