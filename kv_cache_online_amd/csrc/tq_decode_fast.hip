@@ -381,7 +381,7 @@ __device__ inline float score_sum(v4i c, int32_t KH, int32_t KL) {
   return fmaf(static_cast<float>(hi - KH), 131072.0f, static_cast<float>(2 * lo - KL));
 }
 
-template <int D, int RB, int BQK, int BQV>
+template <int D, int RB, int BQK, int BQV, bool DEEP>
 struct SplitShape {
   static constexpr int C = D / 64, W = D / 32, NB = D / 64, NW = D / 128, G = 4 * RB;
   static constexpr int PK = BQK == 3 ? 4 : BQK, PV = BQV == 3 ? 4 : BQV;
@@ -394,17 +394,17 @@ struct SplitShape {
   static constexpr int SLOT = K_BYTES > V_BYTES ? K_BYTES : V_BYTES;
   static constexpr int NI_K = (BQK + 1) * NW + 2, NI_V = (BQV + 1) * NW;  // loads per chunk
   static constexpr int NI_MIN = NI_K < NI_V ? NI_K : NI_V;
-  // Ring slots per wave and value operand buffers (round parity).  With two
-  // head blocks the split pass is bound by its ALU work, so it takes the smaller
-  // LDS footprint that fits three work-groups per CU; with one it is bound by
-  // memory latency and keeps two chunks in flight per wave.
-  static constexpr int SLOTS = RB == 1 ? 3 : 2;
-  static constexpr int AWP = RB == 1 ? 2 : 1;
+  // Ring slots per wave and value operand buffers (round parity).  DEEP (one
+  // head block, few work-groups: latency-bound) keeps two chunks in flight per
+  // wave; otherwise the smaller LDS footprint fits more work-groups per CU, which
+  // hides more (three or four per CU).
+  static constexpr int SLOTS = DEEP ? 3 : 2;
+  static constexpr int AWP = DEEP ? 2 : 1;
 };
 
-template <int D, int RB, int BQK, int BQV>
+template <int D, int RB, int BQK, int BQV, bool DEEP>
 __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
-  using P = SplitShape<D, RB, BQK, BQV>;
+  using P = SplitShape<D, RB, BQK, BQV, DEEP>;
   constexpr int C = P::C, W = P::W, NB = P::NB, NW = P::NW, G = P::G, PK = P::PK, PV = P::PV;
   constexpr int KREC = P::KREC, KSREC = P::KSREC, VREC = P::VREC, VSREC = P::VSREC, AWP = P::AWP;
   constexpr int kSlots = P::SLOTS;
@@ -1034,24 +1034,24 @@ __global__ __launch_bounds__(512) void decode_merge_grouped(DecodeArgs a, int nq
   }
 }
 
-template <int D, int RB, int BQK>
+template <int D, int RB, int BQK, bool DEEP>
 int launch_partial_bv(int bqv, const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hkv, a.batch);
   if (a.split_tokens > kMaxT * 256 || a.n_split > kMaxSplits) return 1;
   switch (bqv) {
-    case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1>), grid, dim3(256), 0, s, a); return 0;
-    case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2>), grid, dim3(256), 0, s, a); return 0;
-    case 3: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 3>), grid, dim3(256), 0, s, a); return 0;
+    case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1, DEEP>), grid, dim3(256), 0, s, a); return 0;
+    case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2, DEEP>), grid, dim3(256), 0, s, a); return 0;
+    case 3: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 3, DEEP>), grid, dim3(256), 0, s, a); return 0;
     default: return 1;
   }
 }
 
-template <int D, int RB>
+template <int D, int RB, bool DEEP>
 int launch_partial(const DecodeArgs &a, hipStream_t s) {
   switch (a.k.bq) {
-    case 1: return launch_partial_bv<D, RB, 1>(a.v.bq, a, s);
-    case 2: return launch_partial_bv<D, RB, 2>(a.v.bq, a, s);
-    case 3: return launch_partial_bv<D, RB, 3>(a.v.bq, a, s);
+    case 1: return launch_partial_bv<D, RB, 1, DEEP>(a.v.bq, a, s);
+    case 2: return launch_partial_bv<D, RB, 2, DEEP>(a.v.bq, a, s);
+    case 3: return launch_partial_bv<D, RB, 3, DEEP>(a.v.bq, a, s);
     default: return 1;
   }
 }
@@ -1062,7 +1062,10 @@ int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
   if (nq >= 512)
     hipLaunchKernelGGL(decode_qprep_grouped<D>, dim3((nq + 7) / 8 * (2 * D / 64)), dim3(256), 0, s, a, int(nq));
   else hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
-  int e = rb == 1 ? launch_partial<D, 1>(a, s) : launch_partial<D, 2>(a, s);
+  // one head block and at most about two work-groups per CU: the deep ring
+  const bool deep = int64_t(a.n_split) * a.Hkv * a.batch <= 1024;
+  int e = rb == 2 ? launch_partial<D, 2, false>(a, s) : deep ? launch_partial<D, 1, true>(a, s)
+                                                              : launch_partial<D, 1, false>(a, s);
   if (e) return e;
   // few splits per head: the projection matrix is the larger read, so heads share it
   if (nq >= 512 && a.n_split <= 64)
