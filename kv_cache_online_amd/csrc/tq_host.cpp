@@ -418,7 +418,7 @@ int tq_quantize_kv(const tq_config *cfg, const void *k, const void *v, tq_dtype 
     a.rot_hml = reinterpret_cast<const uint16_t *>(prep + L.rot_hml);
     a.st_hml = reinterpret_cast<const uint16_t *>(prep + L.st_hml);
     a.status = status;
-    const bool fast = cfg->d == 128 && cb_symmetric(a.t.cb);
+    const bool fast = (cfg->d == 128 || (cfg->d == 256 && dt == TQ_BF16)) && cb_symmetric(a.t.cb);
     const int rc = fast ? tq::launch_quantize_fast(cfg->d, a, stream) : tq::launch_quantize(cfg->d, a, stream);
     if (rc != 0) return TQ_ERR_LAUNCH;
   }

@@ -1,4 +1,5 @@
-// Matrix-core quantize for d = m = 128 on gfx950.
+// Matrix-core quantize for d = m = 128 (and, further down, d = m = 256 with
+// bf16 input) on gfx950.
 //
 // Method: ast-softpro.ru, "Технология TurboQuant и её применение с локальными
 // LLM", section 1.2 "Как работает TurboQuant" -- stage 1 rotates x by Pi and
@@ -86,6 +87,9 @@ __host__ inline FastDiv make_fastdiv(uint32_t d) {
 
 __device__ inline uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.s; }
 
+// Tile `tile` of TT vectors: tiles run over (sequence, head, k), and tile k of a
+// sequence starts at the 32-slot boundary at or below its first slot, plus TT k.
+template <int TT>
 __device__ inline Tile tile_at(const QuantArgs &a, uint32_t tile, FastDiv ftpb, FastDiv fh) {
   Tile T;
   const uint32_t bh = fdiv(tile, ftpb);
@@ -94,8 +98,8 @@ __device__ inline Tile tile_at(const QuantArgs &a, uint32_t tile, FastDiv ftpb, 
   T.h = static_cast<int>(bh - uint32_t(T.b) * fh.d);
   const int64_t d0 = a.dst[T.b];
   const int sh = static_cast<int>(d0 & 31);
-  T.base = (d0 - sh) + 32 * int64_t(k);
-  T.t0 = 32 * k - sh;
+  T.base = (d0 - sh) + TT * int64_t(k);
+  T.t0 = TT * k - sh;
   return T;
 }
 
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
   uint32_t tile = blockIdx.x;
   Tile T{};
   if (tile < n_tiles) {
-    T = tile_at(a, tile, ftpb, fh);
+    T = tile_at<QT>(a, tile, ftpb, fh);
     load_rows<F32>(a, T, v, c16, xr);
   }
   for (; tile < n_tiles; tile += gridDim.x) {
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
     for (int i = 0; i < NV; ++i) xc[i] = xr[i];
     const uint32_t nxt = tile + gridDim.x;
     if (nxt < n_tiles) {
-      T = tile_at(a, nxt, ftpb, fh);
+      T = tile_at<QT>(a, nxt, ftpb, fh);
       load_rows<F32>(a, T, v, c16, xr);
     }
     if (cur.t0 >= a.n_new) continue;  // no token falls in this tile (uniform)
@@ -557,11 +561,450 @@ int launch_q(const QuantArgs &a, hipStream_t s) {
   return hipGetLastError() != hipSuccess;
 }
 
+// ===========================================================================
+// d = m = 256.  The bf16 pieces of Pi and S~ (512 or 640 KB) exceed what a CU
+// holds in registers and LDS together, so they stream from L2 (every CU reads
+// the same matrices, which stay resident there) into registers: a 32-column
+// slice of the wave's rows at a time, WPD slices ahead of the products.  The
+// tile grows to 128 vectors (four 32-slot blocks), so each matrix element
+// fetched serves 128 products, and the input tile and then the residual's two
+// pieces share one LDS region.  Work-group: 8 waves, one per CU; wave w owns
+// coordinates and sketch rows 32w .. 32w+31.  bf16 input only (exact in one
+// piece); Pi takes its hi and mid pieces, and lo too at b' = 3, where the
+// residual is smallest relative to ||x|| and ||r||'s tolerance needs it.
+// Phases per tile as above: A (input to LDS, norms), B (z = Pi x, cells,
+// residual), D (sketch), E (records); the next tile's input is loaded into
+// registers during D, after the first sketch slices, so the in-order
+// completion of loads does not make those slices wait for HBM.
+// ===========================================================================
+constexpr int WD = 256;      // d = m
+constexpr int WT = 128;      // vectors per tile
+constexpr int WW = 8;        // waves per work-group
+constexpr int WN = 64 * WW;  // threads per work-group
+constexpr int WXS = WD + 8;  // bf16 row stride of the operand tiles (elements)
+constexpr int WPD = 2;       // matrix slices in flight ahead of the products
+
+template <int BQ>
+struct WSmem {
+  union {
+    __align__(16) uint16_t xs[WT][WXS];     // input (bf16 bits)
+    __align__(16) uint16_t rp[2][WT][WXS];  // residual: hi and mid pieces
+  } u;
+  __align__(16) float vth[WT][8];                // per vector: ||x|| t_k at 0..2, ||x||~ c_k at 4..7
+  __align__(16) float rr[WW][WT];                // ||rho||^2 over each wave's coordinates
+  __align__(16) uint16_t wst[BQ + 1][4][WD][2];  // words (plane, block, coordinate); plane BQ: signs
+  __align__(16) uint32_t nub[WT];                // fp16 bits of ||x||
+  __align__(16) uint32_t scl[WT];                // nu bits | rho bits << 16
+};
+
+// PlaneBits over the four 32-slot blocks of a tile: pk[blk] gathers the masks
+// of column blocks 2 blk and 2 blk + 1 in the lane order PlaneBits uses.
+struct PlaneBits4 {
+  uint32_t pk[4] = {0u, 0u, 0u, 0u};
+  __device__ inline void put(uint64_t m, int rb, int cb, int r) {
+    const int l = rb * 16 + r * 4 + (cb & 1) * 2;
+    pk[cb >> 1] = wlane(static_cast<uint32_t>(m), l, pk[cb >> 1]);
+    pk[cb >> 1] = wlane(static_cast<uint32_t>(m >> 32), l + 1, pk[cb >> 1]);
+  }
+  __device__ inline void store(uint16_t (*w)[WD][2], int lane, int c0) const {
+    if (lane < 32) {
+      const int rb = lane >> 4, r = (lane >> 2) & 3, g2 = (lane >> 1) & 1, hh = lane & 1;
+      const int c = c0 + 16 * rb + 8 * hh + r;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        w[blk][c][g2] = static_cast<uint16_t>(pk[blk]);
+        w[blk][c + 4][g2] = static_cast<uint16_t>(pk[blk] >> 16);
+      }
+    }
+  }
+};
+
+// Row v of a 128-vector tile, 16-byte chunks 4 i + q4 (i = 0..7): four lanes
+// read 64 contiguous bytes of a row per instruction.  Zeros outside the tokens.
+__device__ inline void load_rows_w(const QuantArgs &a, const Tile &T, int v, int q4, uint4 *r) {
+  const int tok = T.t0 + v;
+  if (tok >= 0 && tok < a.n_new) {
+    const size_t row = (size_t(T.b) * a.H + T.h) * size_t(a.n_new) + tok;
+    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.t.x) + row * WD) + q4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = p[4 * i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// One 32-column slice (columns 32 kc + 8 lg .. + 7) of the wave's two row
+// blocks of NP pieces of a 256 x 256 matrix split as [3][256][256], through a
+// buffer resource: the lane's byte offset voff in a VGPR, the slice's in an SGPR.
+template <int NP>
+__device__ inline void load_slice(__amdgpu_buffer_rsrc_t m, int voff, int kc, bf16x8 (*dst)[2]) {
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      dst[p][rb] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(m, voff, 2 * ((p * WD + 16 * rb) * WD + 32 * kc), 0));
+}
+
+template <int BQ, int NPI>
+__global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_tiles, FastDiv ftpb, FastDiv fh) {
+  constexpr int L = 1 << BQ;
+  constexpr int K = L / 2 - 1;  // positive boundaries
+  __shared__ WSmem<BQ> sm;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, li = lane & 15, lg = lane >> 4;
+  const int v = t >> 2, q4 = t & 3;  // phase A: row v, chunks 4 i + q4
+  const int cw = 32 * w;             // first coordinate / sketch row of this wave
+  const bool sk = a.t.sketch != 0;
+  // lane (li, lg) of a slice: rows cw + 16 rb + li, columns 32 kc + 8 lg .. + 7
+  const __amdgpu_buffer_rsrc_t prot =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.rot_hml), 0, 3 * WD * WD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t pst =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.st_hml), 0, 3 * WD * WD * 2, 0x00020000);
+  const int moff = 2 * ((cw + li) * WD + 8 * lg);
+
+  float tpos[K > 0 ? K : 1], cpos[K + 1];
+#pragma unroll
+  for (int k = 0; k < K; ++k) tpos[k] = a.t.cb.thr[L / 2 + k];
+#pragma unroll
+  for (int k = 0; k <= K; ++k) cpos[k] = a.t.cb.cen[L / 2 + k];
+
+  uint32_t flags = 0;
+  uint4 xr[8];
+  uint32_t tile = blockIdx.x;
+  Tile T{};
+  if (tile < n_tiles) {
+    T = tile_at<WT>(a, tile, ftpb, fh);
+    load_rows_w(a, T, v, q4, xr);
+  }
+  for (; tile < n_tiles; tile += gridDim.x) {
+    const Tile cur = T;
+    const uint32_t nxt = tile + gridDim.x;
+    if (cur.t0 >= a.n_new) {  // no token falls in this tile (uniform)
+      if (nxt < n_tiles) {
+        T = tile_at<WT>(a, nxt, ftpb, fh);
+        load_rows_w(a, T, v, q4, xr);
+      }
+      continue;
+    }
+    bf16x8 pa[WPD + 1][NPI][2];  // ring of slices of Pi
+#pragma unroll
+    for (int kc = 0; kc < WPD; ++kc) load_slice<NPI>(prot, moff, kc, pa[kc]);
+
+    // ---------------------------------------------------------------- A --
+    {
+      const uint32_t *u = reinterpret_cast<const uint32_t *>(xr);
+      float ssf = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const bf16x2 b2 = __builtin_bit_cast(bf16x2, u[i]);
+        ssf = __builtin_amdgcn_fdot2_f32_bf16(b2, b2, ssf, false);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4 *>(&sm.u.xs[v][8 * (4 * i + q4)]) = xr[i];
+      ssf += __shfl_xor(ssf, 1, kWave);
+      ssf += __shfl_xor(ssf, 2, kWave);
+      float nu;
+      bool nonfinite = false;
+      if (__builtin_expect(!isfinite(ssf), 0)) {
+        // rare: an element is not finite, or a float32 square overflowed
+        double sd = 0.0;
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+          const float xi = __uint_as_float((i & 1) ? (u[i >> 1] & 0xFFFF0000u) : (u[i >> 1] << 16));
+          bad |= !isfinite(xi);
+          sd = fma(double(xi), double(xi), sd);
+        }
+#pragma unroll
+        for (int o = 1; o < 4; o <<= 1) {
+          sd += __shfl_xor(sd, o, kWave);
+          bad |= __shfl_xor(static_cast<int>(bad), o, kWave) != 0;
+        }
+        nonfinite = bad;
+        nu = static_cast<float>(sqrt(sd));
+      } else {
+        nu = __builtin_amdgcn_sqrtf(ssf);
+      }
+      if (q4 == 0) {
+        bool over = false;
+        const uint32_t nb = f16_bits_f32(nu, &over);
+        const float n16 = f16_val(nb);
+        f32x4 th = {INFINITY, INFINITY, INFINITY, INFINITY}, cs = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < K; ++k) th[k] = nu > 0.0f ? nu * tpos[k] : INFINITY;
+#pragma unroll
+        for (int k = 0; k <= K; ++k) cs[k] = n16 * cpos[k];
+        *reinterpret_cast<f32x4 *>(&sm.vth[v][0]) = th;
+        *reinterpret_cast<f32x4 *>(&sm.vth[v][4]) = cs;
+        sm.nub[v] = nb;
+        const int tok = cur.t0 + v;
+        if (tok >= 0 && tok < a.n_new) {
+          if (nonfinite) flags |= TQ_FLAG_NONFINITE_INPUT;
+          if (over) flags |= TQ_FLAG_SCALE_OVERFLOW;
+          if (a.t.dbg) a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2] = nu;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- B --
+    f32x4 acc[2][8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      if (kc + WPD < 8) load_slice<NPI>(prot, moff, kc + WPD, pa[(kc + WPD) % (WPD + 1)]);
+      const int sl = kc % (WPD + 1);
+      // column operands one column block ahead of their products; the fences
+      // keep the scheduler from hoisting every block's operand (registers)
+      bf16x8 xb[2];
+      xb[0] = *reinterpret_cast<const bf16x8 *>(&sm.u.xs[li][32 * kc + 8 * lg]);
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        if (cb < 7) xb[(cb + 1) & 1] = *reinterpret_cast<const bf16x8 *>(&sm.u.xs[16 * (cb + 1) + li][32 * kc + 8 * lg]);
+#pragma unroll
+        for (int p = 0; p < NPI; ++p)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[sl][p][rb], xb[cb & 1], acc[rb][cb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // acc[rb][cb] lane (li, lg) register r: coordinate cw + 16 rb + 4 lg + r of vector 16 cb + li;
+    // it is overwritten with the residual.
+    {
+      PlaneBits4 pb[BQ];
+      float rr[8];
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        const int vv = 16 * cb + li;
+        const f32x4 th = *reinterpret_cast<const f32x4 *>(&sm.vth[vv][0]);
+        const f32x4 cs = *reinterpret_cast<const f32x4 *>(&sm.vth[vv][4]);
+        rr[cb] = 0.0f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float z = acc[rb][cb][r];
+            const float az = fabsf(z);
+            const bool pos = z >= 0.0f;
+            float val = cs[0];
+            uint64_t cm[K > 0 ? K : 1];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+              const bool c = az >= th[k];
+              val = c ? cs[k + 1] : val;
+              cm[k] = __ballot(c);
+            }
+            const float rho = z - (pos ? val : -val);
+            acc[rb][cb][r] = rho;
+            rr[cb] = fmaf(rho, rho, rr[cb]);
+            const uint64_t pm = __ballot(pos);
+            // cell index bits from the thermometer-coded compares, as for d = 128
+#pragma unroll
+            for (int q = 0; q < BQ; ++q) {
+              uint64_t bits = pm;
+              if (q < BQ - 1) {
+                uint64_t mq = 0;
+#pragma unroll
+                for (int k = 1; k <= K; ++k)
+                  if ((k & ((1 << q) - 1)) == 0) mq ^= cm[k - 1];
+                bits = ~(mq ^ pm);
+              }
+              pb[q].put(bits, rb, cb, r);
+            }
+          }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        float x = rr[cb];
+        x += __shfl_xor(x, 16, kWave);
+        x += __shfl_xor(x, 32, kWave);
+        if (lg == 0) sm.rr[w][16 * cb + li] = x;
+      }
+#pragma unroll
+      for (int q = 0; q < BQ; ++q) pb[q].store(sm.wst[q], lane, cw);
+    }
+    __syncthreads();  // every wave is done with the input tile
+    bf16x8 ps[WPD + 1][2][2];  // ring of slices of S~ (hi, mid)
+    if (sk) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+          const f32x4 rho = acc[rb][cb];
+          const uint32_t h01 = cvt_pk_bf16(rho[0], rho[1]), h23 = cvt_pk_bf16(rho[2], rho[3]);
+          const uint32_t m01 =
+              cvt_pk_bf16(rho[0] - __uint_as_float(h01 << 16), rho[1] - __uint_as_float(h01 & 0xFFFF0000u));
+          const uint32_t m23 =
+              cvt_pk_bf16(rho[2] - __uint_as_float(h23 << 16), rho[3] - __uint_as_float(h23 & 0xFFFF0000u));
+          const int c = cw + 16 * rb + 4 * lg, vv = 16 * cb + li;
+          *reinterpret_cast<uint2 *>(&sm.u.rp[0][vv][c]) = make_uint2(h01, h23);
+          *reinterpret_cast<uint2 *>(&sm.u.rp[1][vv][c]) = make_uint2(m01, m23);
+        }
+#pragma unroll
+      for (int kc = 0; kc < WPD; ++kc) load_slice<2>(pst, moff, kc, ps[kc]);
+    }
+    if (nxt < n_tiles) {
+      T = tile_at<WT>(a, nxt, ftpb, fh);
+      load_rows_w(a, T, v, q4, xr);
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- D --
+    {
+      uint32_t rbits = 0;
+      if (sk) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) {
+          if (kc + WPD < 8) load_slice<2>(pst, moff, kc + WPD, ps[(kc + WPD) % (WPD + 1)]);
+          const int sl = kc % (WPD + 1);
+          bf16x8 bh[2], bm[2];
+          bh[0] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[0][li][32 * kc + 8 * lg]);
+          bm[0] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[1][li][32 * kc + 8 * lg]);
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb) {
+            if (cb < 7) {
+              bh[(cb + 1) & 1] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[0][16 * (cb + 1) + li][32 * kc + 8 * lg]);
+              bm[(cb + 1) & 1] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[1][16 * (cb + 1) + li][32 * kc + 8 * lg]);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps[sl][0][rb], bh[cb & 1], acc[rb][cb], 0, 0, 0);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps[sl][1][rb], bh[cb & 1], acc[rb][cb], 0, 0, 0);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps[sl][0][rb], bm[cb & 1], acc[rb][cb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        PlaneBits4 pbs;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pbs.put(__ballot(acc[rb][cb][r] >= 0.0f), rb, cb, r);
+        pbs.store(sm.wst[BQ], lane, cw);
+        if (t < WT) {
+          float rr = 0.0f;
+#pragma unroll
+          for (int ww = 0; ww < WW; ++ww) rr += sm.rr[ww][t];
+          const float rho = __builtin_amdgcn_sqrtf(rr);
+          bool over = false;
+          rbits = f16_bits_f32(rho, &over);
+          const int tok = cur.t0 + t;
+          if (tok >= 0 && tok < a.n_new) {
+            if (over) flags |= TQ_FLAG_SCALE_OVERFLOW;
+            if (a.t.dbg) a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = rho;
+          }
+        }
+      } else if (t < WT) {
+        const int tok = cur.t0 + t;
+        if (tok >= 0 && tok < a.n_new && a.t.dbg)
+          a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = 0.0f;
+      }
+      if (t < WT) sm.scl[t] = sm.nub[t] | (rbits << 16);
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- E --
+    {
+      // block blk holds slots base + 32 blk ..; its tokens t0 + 32 blk + j, j in [lo, hi)
+      uint32_t vm[4];
+      bool inr[4];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int tb = cur.t0 + 32 * blk;
+        const int lo = tb < 0 ? -tb : 0;
+        const int hi = a.n_new - tb < 32 ? a.n_new - tb : 32;
+        vm[blk] = hi <= lo ? 0u : hi - lo >= 32 ? 0xFFFFFFFFu : (((1u << (hi - lo)) - 1u) << lo);
+        const int64_t sb = cur.base + 32 * blk;  // base and cap are multiples of 32
+        inr[blk] = sb >= 0 && sb < a.t.cap;
+        if (vm[blk] != 0u && !inr[blk]) flags |= TQ_FLAG_OUT_OF_RANGE;
+      }
+      const int npl = BQ + (sk ? 1 : 0);
+      const int64_t hs0 = int64_t(cur.h) * a.t.cap + cur.base;
+      if (t < WT && ((vm[t >> 5] >> (t & 31)) & 1) && inr[t >> 5])
+        *reinterpret_cast<uint32_t *>(a.t.scl + (hs0 + t) * 2) = sm.scl[t];
+      if (a.t.layout == TQ_LAYOUT_BLOCK32) {
+        // the (plane, block, coordinate) words are the value layout's words
+        const int64_t b0 = int64_t(cur.h) * (a.t.cap / 32) + (cur.base >> 5);
+        for (int c = t; c < npl * 4 * WD; c += WN) {
+          const int pl = c / (4 * WD), blk = (c / WD) & 3, cc = c % WD;
+          const uint32_t m = vm[blk];
+          if (m == 0u || !inr[blk]) continue;
+          const uint32_t word = *reinterpret_cast<const uint32_t *>(&sm.wst[pl][blk][cc][0]);
+          uint32_t *dw = pl < BQ ? a.t.idx + ((b0 + blk) * BQ + pl) * WD + cc : a.t.sgn + (b0 + blk) * WD + cc;
+          if (m == 0xFFFFFFFFu) {
+            *dw = word;
+          } else {
+            atomicAnd(dw, ~m);
+            atomicOr(dw, word & m);
+          }
+        }
+      } else {
+        // token-major: transpose each 32 x 32 block (plane, block, coordinate word) to per-slot words
+        for (int b2 = 0; b2 < npl * 32; b2 += 2 * WW) {
+          const int bid = b2 + 2 * w + (lane >> 5), row = lane & 31;
+          const int pl = bid >> 5, blk = (bid >> 3) & 3, wd = bid & 7;
+          uint32_t word = *reinterpret_cast<const uint32_t *>(&sm.wst[pl][blk][32 * wd + row][0]);
+          word = transpose32(word, row);  // lane row now holds slot base + 32 blk + row
+          if (((vm[blk] >> row) & 1) && inr[blk]) {
+            const int64_t slot = hs0 + 32 * blk + row;
+            uint32_t *dw = pl < BQ ? a.t.idx + (slot * BQ + pl) * (WD / 32) + wd : a.t.sgn + slot * (WD / 32) + wd;
+            *dw = word;
+          }
+        }
+      }
+    }
+  }
+  if (a.status) {
+    const uint64_t f1 = __ballot(flags & 1u), f2 = __ballot(flags & 2u), f4 = __ballot(flags & 4u);
+    const uint32_t f = (f1 ? 1u : 0u) | (f2 ? 2u : 0u) | (f4 ? 4u : 0u);
+    if (lane == 0 && f) atomicOr(a.status, f);
+  }
+}
+
+template <int BQ>
+int launch_w(const QuantArgs &a, hipStream_t s) {
+  const int64_t tpb = (int64_t(a.n_new) + 31 + WT - 1) / WT;
+  const int64_t n_tiles = int64_t(a.batch) * a.H * tpb;
+  if (n_tiles >= (int64_t(1) << 31)) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const unsigned grid = static_cast<unsigned>(n_tiles < cus ? n_tiles : cus);
+  if (grid == 0) return 0;
+  constexpr int NPI = BQ == 3 ? 3 : 2;
+  hipLaunchKernelGGL((quantize_wide<BQ, NPI>), dim3(grid), dim3(WN), 0, s, a, static_cast<uint32_t>(n_tiles),
+                     make_fastdiv(static_cast<uint32_t>(tpb)), make_fastdiv(static_cast<uint32_t>(a.H)));
+  return hipGetLastError() != hipSuccess;
+}
+
 }  // namespace
 
 int launch_quantize_fast(int d, const QuantArgs &a, hipStream_t s) {
-  if (d != QD) return 1;
   const bool f32 = a.dtype == TQ_F32;
+  if (d == WD && !f32) {
+    switch (a.t.bq) {
+      case 1: return launch_w<1>(a, s);
+      case 2: return launch_w<2>(a, s);
+      case 3: return launch_w<3>(a, s);
+      default: return 1;
+    }
+  }
+  if (d != QD) return 1;
   switch (a.t.bq) {
     case 1: return f32 ? launch_q<1, true>(a, s) : launch_q<1, false>(a, s);
     case 2: return f32 ? launch_q<2, true>(a, s) : launch_q<2, false>(a, s);
