@@ -186,9 +186,11 @@ def test_reduced_workloads(wid, batch, T):
     assert run.status() == 0
 
 
-def test_ragged_incremental_reduced():
-    """Ragged lengths, then one appended token per sequence at its current end."""
-    w = W.WORKLOADS[4]
+@pytest.mark.parametrize("wid", [4, 5])
+def test_ragged_incremental_reduced(wid):
+    """Ragged lengths, then one appended token per sequence at its current end
+    (workload 5: the d = 256 kernels, whose tiles span four 32-slot blocks)."""
+    w = W.WORKLOADS[wid]
     lens = np.random.default_rng(3).integers(1, 700, size=5)
     run = Run(w, batch=5, lens=lens, extra=1)
     K = run.K.copy()
@@ -204,7 +206,7 @@ def test_ragged_incremental_reduced():
     dst = run.starts + lens
     _log("ragged reduced: incremental quantize")
     dbg = run.quantize(K=newk, V=newv, dst=dst)
-    check_quantize(run, dbg, K=newk, V=newv, starts=dst, label="w4-incremental")
+    check_quantize(run, dbg, K=newk, V=newv, starts=dst, label=f"w{wid}-incremental")
     # the cache now holds len + 1 tokens per sequence
     for s in range(5):
         L = lens[s]
@@ -212,13 +214,14 @@ def test_ragged_incremental_reduced():
         run.V[s, :, L] = newv[s, :, 0]
     lens1 = lens + 1
     out = run.decode(lens=lens1)
-    check_decode(run, out, lens=lens1, label="w4-reduced")
+    check_decode(run, out, lens=lens1, label=f"w{wid}-reduced")
     assert run.status() == 0
 
 
-def test_mse_only_and_asymmetric_bits():
-    """Keys with 3+1 bits, values MSE-only with 2 bits (and the reverse)."""
-    w = W.WORKLOADS[2]
+@pytest.mark.parametrize("wid", [2, 5])
+def test_mse_only_and_asymmetric_bits(wid):
+    """Keys with 3+1 bits, values MSE-only with 2 bits (and the reverse), at d = 128 and 256."""
+    w = W.WORKLOADS[wid]
     for kb, vb, ks, vs in ((3, 2, 1, 0), (1, 3, 0, 1)):
         run = Run(w, batch=1, n_tokens=300, k_bits=kb, v_bits=vb, k_sketch=ks, v_sketch=vs)
         _log(f"asymmetric k{kb}{'+s' if ks else ''} v{vb}{'+s' if vs else ''}")
@@ -240,8 +243,9 @@ def test_exact_sphere_law_codebook(wid, batch, n_tokens):
 
 
 # -------------------------------------------------------------- edge cases ---
-def test_edge_cases():
-    w = W.small(W.WORKLOADS[2], n_kv_heads=1, n_q_heads=4)
+@pytest.mark.parametrize("wid", [2, 5])
+def test_edge_cases(wid):
+    w = W.small(W.WORKLOADS[wid], n_kv_heads=1, n_q_heads=4)
     run = Run(w, batch=3, n_tokens=64)
     K, V = run.K.copy(), run.V.copy()
     K[0, 0, 5] = 0                                   # zero vector
@@ -279,8 +283,9 @@ def test_edge_cases():
     assert run.status() & 4
 
 
-def test_determinism():
-    w = W.WORKLOADS[2]
+@pytest.mark.parametrize("wid", [2, 5])
+def test_determinism(wid):
+    w = W.WORKLOADS[wid]
     run = Run(w, batch=1, n_tokens=512)
     run.quantize()
     a = [x.copy() for c in run.host_caches() for x in c if x is not None]
