@@ -574,27 +574,47 @@ int launch_q(const QuantArgs &a, hipStream_t s) {
 // residual is smallest relative to ||x|| and ||r||'s tolerance needs it.
 // Phases per tile as above: A (input to LDS, norms), B (z = Pi x, cells,
 // residual), D (sketch), E (records); the next tile's input is loaded into
-// registers during D, after the first sketch slices, so the in-order
-// completion of loads does not make those slices wait for HBM.
+// registers after the sketch's products, so that the in-order completion of
+// loads never makes a matrix slice wait for HBM.
 // ===========================================================================
 constexpr int WD = 256;      // d = m
 constexpr int WT = 128;      // vectors per tile
 constexpr int WW = 8;        // waves per work-group
 constexpr int WN = 64 * WW;  // threads per work-group
-constexpr int WXS = WD + 8;  // bf16 row stride of the operand tiles (elements)
 constexpr int WPD = 2;       // matrix slices in flight ahead of the products
+constexpr int WPF = 2;       // column operand reads in flight ahead of the products
 
 template <int BQ>
 struct WSmem {
   union {
-    __align__(16) uint16_t xs[WT][WXS];     // input (bf16 bits)
-    __align__(16) uint16_t rp[2][WT][WXS];  // residual: hi and mid pieces
+    __align__(16) uint16_t xs[WT * WD];     // input (bf16 bits), swizzled rows
+    __align__(16) uint16_t rp[2][WT * WD];  // residual: hi and mid pieces, swizzled rows
   } u;
   __align__(16) float vth[WT][8];                // per vector: ||x|| t_k at 0..2, ||x||~ c_k at 4..7
   __align__(16) float rr[WW][WT];                // ||rho||^2 over each wave's coordinates
   __align__(16) uint16_t wst[BQ + 1][4][WD][2];  // words (plane, block, coordinate); plane BQ: signs
   __align__(16) uint32_t nub[WT];                // fp16 bits of ||x||
   __align__(16) uint32_t scl[WT];                // nu bits | rho bits << 16
+};
+
+// Element index of 16-byte chunk `chunk` (0..31) of row `row` in an operand
+// tile: rows are unpadded and the chunk index is XORed with the row's low four
+// bits.  An MFMA operand read (16 rows, four consecutive chunks) then spreads
+// over all LDS banks; a padded row stride of 16 bytes costs about four stall
+// cycles per 128-bit read on gfx950 (measured with the bank-conflict counter).
+__device__ inline int swz(int row, int chunk) { return row * WD + 8 * (chunk ^ (row & 15)); }
+
+// The MFMA column operand of step (kc, cb): row 16 cb + li, chunk 4 kc + lg.
+// With li = 4 lh + ll the chunk is 4 (kc ^ lh) + (lg ^ ll), so the element
+// index is base[kc & 3] + WD * 16 cb + 32 (kc & 4): four per-lane bases, and
+// everything else an immediate offset of the LDS read.
+struct OpBase {
+  int b[4];
+  __device__ inline OpBase(int li, int lg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = li * WD + 32 * (j ^ (li >> 2)) + 8 * (lg ^ (li & 3));
+  }
+  __device__ inline int at(int kc, int cb) const { return b[kc & 3] + WD * 16 * cb + 32 * (kc & 4); }
 };
 
 // PlaneBits over the four 32-slot blocks of a tile: pk[blk] gathers the masks
@@ -662,6 +682,7 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
   const __amdgpu_buffer_rsrc_t pst =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.st_hml), 0, 3 * WD * WD * 2, 0x00020000);
   const int moff = 2 * ((cw + li) * WD + 8 * lg);
+  const OpBase ob(li, lg);
 
   float tpos[K > 0 ? K : 1], cpos[K + 1];
 #pragma unroll
@@ -701,7 +722,7 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
         ssf = __builtin_amdgcn_fdot2_f32_bf16(b2, b2, ssf, false);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4 *>(&sm.u.xs[v][8 * (4 * i + q4)]) = xr[i];
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4 *>(&sm.u.xs[swz(v, 4 * i + q4)]) = xr[i];
       ssf += __shfl_xor(ssf, 1, kWave);
       ssf += __shfl_xor(ssf, 2, kWave);
       float nu;
@@ -754,22 +775,28 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // Column operands WPF steps ahead of their products over the 64 (kc, cb)
+    // steps; the fences keep the scheduler from hoisting every step's operand
+    // (registers).
+    bf16x8 xb[WPF + 1];
+#pragma unroll
+    for (int s0 = 0; s0 < WPF; ++s0)
+      xb[s0] = *reinterpret_cast<const bf16x8 *>(&sm.u.xs[ob.at(s0 >> 3, s0 & 7)]);
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       if (kc + WPD < 8) load_slice<NPI>(prot, moff, kc + WPD, pa[(kc + WPD) % (WPD + 1)]);
       const int sl = kc % (WPD + 1);
-      // column operands one column block ahead of their products; the fences
-      // keep the scheduler from hoisting every block's operand (registers)
-      bf16x8 xb[2];
-      xb[0] = *reinterpret_cast<const bf16x8 *>(&sm.u.xs[li][32 * kc + 8 * lg]);
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
-        if (cb < 7) xb[(cb + 1) & 1] = *reinterpret_cast<const bf16x8 *>(&sm.u.xs[16 * (cb + 1) + li][32 * kc + 8 * lg]);
+        const int st = 8 * kc + cb, sn = st + WPF;
+        if (sn < 64)
+          xb[sn % (WPF + 1)] = *reinterpret_cast<const bf16x8 *>(&sm.u.xs[ob.at(sn >> 3, sn & 7)]);
 #pragma unroll
         for (int p = 0; p < NPI; ++p)
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[sl][p][rb], xb[cb & 1], acc[rb][cb], 0, 0, 0);
+            acc[rb][cb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[sl][p][rb], xb[st % (WPF + 1)], acc[rb][cb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -841,14 +868,15 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
               cvt_pk_bf16(rho[0] - __uint_as_float(h01 << 16), rho[1] - __uint_as_float(h01 & 0xFFFF0000u));
           const uint32_t m23 =
               cvt_pk_bf16(rho[2] - __uint_as_float(h23 << 16), rho[3] - __uint_as_float(h23 & 0xFFFF0000u));
-          const int c = cw + 16 * rb + 4 * lg, vv = 16 * cb + li;
-          *reinterpret_cast<uint2 *>(&sm.u.rp[0][vv][c]) = make_uint2(h01, h23);
-          *reinterpret_cast<uint2 *>(&sm.u.rp[1][vv][c]) = make_uint2(m01, m23);
+          // coordinates cw + 16 rb + 4 lg .. + 3: half lg & 1 of chunk 4 w + 2 rb + lg / 2
+          const int e = swz(16 * cb + li, 4 * w + 2 * rb + (lg >> 1)) + 4 * (lg & 1);
+          *reinterpret_cast<uint2 *>(&sm.u.rp[0][e]) = make_uint2(h01, h23);
+          *reinterpret_cast<uint2 *>(&sm.u.rp[1][e]) = make_uint2(m01, m23);
         }
 #pragma unroll
       for (int kc = 0; kc < WPD; ++kc) load_slice<2>(pst, moff, kc, ps[kc]);
     }
-    if (nxt < n_tiles) {
+    if (!sk && nxt < n_tiles) {
       T = tile_at<WT>(a, nxt, ftpb, fh);
       load_rows_w(a, T, v, q4, xr);
     }
@@ -862,30 +890,41 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int cb = 0; cb < 8; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        bf16x8 bh[WPF + 1], bm[WPF + 1];
+#pragma unroll
+        for (int s0 = 0; s0 < WPF; ++s0) {
+          bh[s0] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[0][ob.at(s0 >> 3, s0 & 7)]);
+          bm[s0] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[1][ob.at(s0 >> 3, s0 & 7)]);
+        }
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc) {
           if (kc + WPD < 8) load_slice<2>(pst, moff, kc + WPD, ps[(kc + WPD) % (WPD + 1)]);
           const int sl = kc % (WPD + 1);
-          bf16x8 bh[2], bm[2];
-          bh[0] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[0][li][32 * kc + 8 * lg]);
-          bm[0] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[1][li][32 * kc + 8 * lg]);
 #pragma unroll
           for (int cb = 0; cb < 8; ++cb) {
-            if (cb < 7) {
-              bh[(cb + 1) & 1] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[0][16 * (cb + 1) + li][32 * kc + 8 * lg]);
-              bm[(cb + 1) & 1] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[1][16 * (cb + 1) + li][32 * kc + 8 * lg]);
+            const int st = 8 * kc + cb, sn = st + WPF, q = st % (WPF + 1);
+            if (sn < 64) {
+              const int e = ob.at(sn >> 3, sn & 7);
+              bh[sn % (WPF + 1)] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[0][e]);
+              bm[sn % (WPF + 1)] = *reinterpret_cast<const bf16x8 *>(&sm.u.rp[1][e]);
             }
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
-              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps[sl][0][rb], bh[cb & 1], acc[rb][cb], 0, 0, 0);
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps[sl][0][rb], bh[q], acc[rb][cb], 0, 0, 0);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
-              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps[sl][1][rb], bh[cb & 1], acc[rb][cb], 0, 0, 0);
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps[sl][1][rb], bh[q], acc[rb][cb], 0, 0, 0);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
-              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps[sl][0][rb], bm[cb & 1], acc[rb][cb], 0, 0, 0);
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps[sl][0][rb], bm[q], acc[rb][cb], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
           }
+        }
+        // the next tile's input: issued after the last matrix slice, since a
+        // wait for a slice issued later would also wait for these HBM loads
+        if (nxt < n_tiles) {
+          T = tile_at<WT>(a, nxt, ftpb, fh);
+          load_rows_w(a, T, v, q4, xr);
         }
         PlaneBits4 pbs;
 #pragma unroll
