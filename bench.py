@@ -46,9 +46,16 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(prefixes):
+def packed_record_bytes(d, m, bits_mse, sketch):
+    """Bytes of one packed vector in the cache layout: b' index planes of d bits,
+    a sign plane of m bits when the sketch is kept, two fp16 scales."""
+    return bits_mse * d // 8 + (m // 8 if sketch else 0) + 4
+
+
+def traffic_for(prefixes, workload):
     """HBM bytes per call (sum over the call's kernels, each by name prefix) from
-    the committed rocprofv3 counter runs, if they were taken on this source."""
+    the committed rocprofv3 counter runs, if they were taken on this source and
+    this workload."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -56,7 +63,7 @@ def traffic_for(prefixes):
         t = json.load(open(p))
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != source_hash():
+    if t.get("source_hash") != source_hash() or t.get("workload") != workload:
         return None
     ks = t.get("kernels", {})
     total = 0.0
@@ -81,7 +88,7 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, workload):
     """profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of
     this bench and of copy_calibration (counters in KiB per dispatch).  Each
     counter is scaled by bytes / counter of the plain copy: FETCH against the
@@ -108,7 +115,7 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_byt
         if k in write and k.startswith(("quantize", "decode")):
             kernels[k] = {"fetch_bytes": fetch[k] * f_scale, "write_bytes": write[k] * w_scale,
                           "bytes": fetch[k] * f_scale + write[k] * w_scale}
-    out = {"source_hash": source_hash(), "copy_kernel": ck, "copy_bytes": copy_bytes,
+    out = {"source_hash": source_hash(), "workload": workload, "copy_kernel": ck, "copy_bytes": copy_bytes,
            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as fh:
@@ -180,7 +187,8 @@ def main():
                     help="write profiles/traffic.json from rocprofv3 counter CSVs (no GPU)")
     args = ap.parse_args()
     if args.traffic:
-        write_traffic(*args.traffic, copy_bytes=1 << 30)
+        import workloads as W
+        write_traffic(*args.traffic, copy_bytes=1 << 30, workload=W.WORKLOADS[args.workload].name)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -191,7 +199,6 @@ def main():
     import torch
     import workloads as W
     from kv_cache_online_amd.session import TQSession
-    from oracle import record_bytes  # layout arithmetic only, for the byte count
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -207,7 +214,7 @@ def main():
     cap = W.capacity(lens)
     starts = W.seq_starts(lens)
     esize = 4 if w.dtype == "f32" else 2
-    rec = record_bytes(d, w.m, w.bits_mse, w.sketch)
+    rec = packed_record_bytes(d, w.m, w.bits_mse, w.sketch)
     in_bytes = 2 * B * H * T * d * esize
     packed_bytes = 2 * B * H * T * rec
     footprint = in_bytes + 2 * H * cap * rec
@@ -269,19 +276,26 @@ def main():
     q_tf = q_flops / q_avg / 1e12
     roof_dec = {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dec_gbs / HBM_PEAK_GBS,
-                "traffic": traffic_for([("decode_qprep", 1), ("decode_partial", 1), ("decode_merge", 1)]),
+                "traffic": traffic_for([("decode_qprep", 1), ("decode_partial", 1), ("decode_merge", 1)], w.name),
                 "kernel": "tq_decode_attention call: query prep + split partials + merge",
                 "bytes_per_launch": packed_bytes, "avg_launch_s": d_avg}
-    # quantize: at algorithmic cost the HBM bytes bound it (the two contractions
-    # at bf16 matrix peak take less time than the bytes at HBM peak)
-    roof_q = {"bound": "hbm", "achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-              "frac": q_gbs / HBM_PEAK_GBS, "traffic": traffic_for([("quantize", 2)]),
-              "kernel": "tq_quantize_kv call: K and V launches", "bytes_per_launch": q_bytes,
-              "avg_launch_s": q_avg,
-              "mfma": {"achieved": q_tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                       "frac": q_tf / BF16_MFMA_PEAK_TFLOPS, "flops_per_launch": q_flops,
-                       "note": "algorithmic 4 d^2 flops per vector; d = 128 executes 6 bf16 passes per "
-                               "vector-pair of contractions (3 for Pi x, 3 for the sketch)"}}
+    # quantize: the bound at algorithmic cost is the larger of the bytes at HBM peak
+    # and the two contractions at bf16 matrix peak (HBM at d = 128, MFMA at d = 256)
+    pieces = 6 if d == 128 or w.bits_mse == 3 else 5
+    note = (f"algorithmic 4 d^2 flops per vector; executed as {pieces} bf16 piece products per vector "
+            f"({pieces - 3} for Pi x, 3 for the sketch)")
+    q_traffic = traffic_for([("quantize", 2)], w.name)
+    hbm_view = {"achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": q_gbs / HBM_PEAK_GBS}
+    mfma_view = {"achieved": q_tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": q_tf / BF16_MFMA_PEAK_TFLOPS, "flops_per_launch": q_flops, "note": note}
+    if q_flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > q_bytes / (HBM_PEAK_GBS * 1e9):
+        roof_q = {"bound": "mfma", **{k: v for k, v in mfma_view.items() if k != "note"}, "traffic": q_traffic,
+                  "kernel": "tq_quantize_kv call: K and V launches", "bytes_per_launch": q_bytes,
+                  "avg_launch_s": q_avg, "note": note, "hbm": hbm_view}
+    else:
+        roof_q = {"bound": "hbm", **hbm_view, "traffic": q_traffic,
+                  "kernel": "tq_quantize_kv call: K and V launches", "bytes_per_launch": q_bytes,
+                  "avg_launch_s": q_avg, "mfma": mfma_view}
     dominant = roof_q if q_avg >= d_avg else roof_dec
     res = {
         "metric": METRIC, "value": dec_gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
