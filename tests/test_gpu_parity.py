@@ -230,6 +230,17 @@ def test_mse_only_and_asymmetric_bits(wid):
         check_decode(run, run.decode(), label=f"k{kb}s{ks}-v{vb}s{vs}")
 
 
+def test_fp32_input_d256():
+    """fp32 K/V at d = 256: the reference-grade quantize (the matrix-core one takes bf16 there)."""
+    w = W.small(W.WORKLOADS[5], dtype="f32")
+    run = Run(w, batch=2, n_tokens=150)
+    _log("fp32 input at d = 256")
+    dbg = run.quantize()
+    check_quantize(run, dbg, label="w5-f32")
+    check_decode(run, run.decode(), label="w5-f32")
+    assert run.status() == 0
+
+
 @pytest.mark.parametrize("wid,batch,n_tokens", [(2, 1, 400), (3, 1, 300), (5, 1, 257)])
 def test_exact_sphere_law_codebook(wid, batch, n_tokens):
     """The codebook of the exact unit-vector coordinate law, end to end: the
