@@ -148,16 +148,41 @@ __device__ inline uint32_t wlane(uint32_t v, int lane, uint32_t old) {
   return static_cast<uint32_t>(tq_writelane_i32(static_cast<int>(v), lane, static_cast<int>(old)));
 }
 
+// The value of lane l ^ s (s = 16, 8, 4, 2, 1).  Below 16 the exchange stays
+// inside a 16-lane row, so it is a DPP move (no LDS round trip): a rotation by
+// 8, quad permutations for 2 and 1, and for 4 a shift up or down by 4 chosen
+// by the lane's own bit 2 (DPP controls as measured on gfx950: row_shl:n reads
+// lane l + n, row_shr:n lane l - n, row_ror:8 lane l ^ 8).
+__device__ inline uint32_t lane_xor(uint32_t a, int s, int lane) {
+  const int v = static_cast<int>(a);
+  switch (s) {
+    case 8: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+    case 4: {
+      const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);
+      const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+      return static_cast<uint32_t>((lane & 4) ? dn : up);
+    }
+    case 2: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+    case 1: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+    default: return static_cast<uint32_t>(__shfl_xor(v, s, kWave));
+  }
+}
+
 // Transpose a 32 x 32 bit matrix held one row per lane (lanes 0-31 and 32-63
-// each hold one matrix): afterwards bit c of lane l is bit l of row c.
+// each hold one matrix): afterwards bit c of lane l is bit l of row c.  Step
+// s exchanges s-bit blocks with lane row ^ s; both candidates are formed and
+// selected, so no step branches.
 __device__ inline uint32_t transpose32(uint32_t a, int row) {
   const uint32_t lo_mask[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
     const int s = 16 >> i;
     const uint32_t m = lo_mask[i];
-    const uint32_t p = static_cast<uint32_t>(__shfl_xor(static_cast<int>(a), s, kWave));
-    a = (row & s) ? ((a & ~m) | ((p >> s) & m)) : ((a & m) | ((p << s) & ~m));
+    const uint32_t p = lane_xor(a, s, row);
+    const bool hi = (row & s) != 0;
+    const uint32_t x = hi ? (p >> s) : (p << s);  // the partner's block, moved into place
+    const uint32_t keep = hi ? ~m : m;             // this lane's own bits
+    a = (a & keep) | (x & ~keep);
   }
   return a;
 }
