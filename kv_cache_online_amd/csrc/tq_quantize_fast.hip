@@ -168,6 +168,16 @@ __device__ inline uint32_t lane_xor(uint32_t a, int s, int lane) {
   }
 }
 
+// Sum of v over the lanes of an aligned group of 2^k lanes (k <= 3), in every
+// lane of the group, by DPP exchanges (lane_xor).
+template <int K>
+__device__ inline float group_sum(float v, int lane) {
+#pragma unroll
+  for (int s = 1 << (K - 1); s > 0; s >>= 1)
+    v += __uint_as_float(lane_xor(__float_as_uint(v), s, lane));
+  return v;
+}
+
 // Transpose a 32 x 32 bit matrix held one row per lane (lanes 0-31 and 32-63
 // each hold one matrix): afterwards bit c of lane l is bit l of row c.  Step
 // s exchanges s-bit blocks with lane row ^ s; both candidates are formed and
@@ -311,8 +321,7 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
         *reinterpret_cast<uint4 *>(&sm.xs[0][v][16 * c16]) = xc[0];
         *reinterpret_cast<uint4 *>(&sm.xs[0][v][16 * c16 + 8]) = xc[1];
       }
-#pragma unroll
-      for (int o = 4; o > 0; o >>= 1) ssf += __shfl_xor(ssf, o, kWave);
+      ssf = group_sum<3>(ssf, lane);
       float nu;
       bool nonfinite = false;
       if (__builtin_expect(!isfinite(ssf), 0)) {
@@ -748,8 +757,7 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4 *>(&sm.u.xs[swz(v, 4 * i + q4)]) = xr[i];
-      ssf += __shfl_xor(ssf, 1, kWave);
-      ssf += __shfl_xor(ssf, 2, kWave);
+      ssf = group_sum<2>(ssf, lane);
       float nu;
       bool nonfinite = false;
       if (__builtin_expect(!isfinite(ssf), 0)) {
