@@ -34,6 +34,7 @@
 #include <cmath>
 
 #include "tq_common.h"
+#include "tq_device.h"
 
 namespace tq {
 namespace {
@@ -607,11 +608,11 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) mloc[rb] = fmaxf(mloc[rb], __shfl_xor(mloc[rb], o, kWave));
+    for (int o = 8; o > 0; o >>= 1) mloc[rb] = fmaxf(mloc[rb], lane_xor_f(mloc[rb], o, lane));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    vnumax = fmaxf(vnumax, __shfl_xor(vnumax, o, kWave));
-    vrhomax = fmaxf(vrhomax, __shfl_xor(vrhomax, o, kWave));
+    vnumax = fmaxf(vnumax, lane_xor_f(vnumax, o, lane));
+    vrhomax = fmaxf(vrhomax, lane_xor_f(vrhomax, o, lane));
   }
   if (col == 0)
 #pragma unroll
@@ -773,7 +774,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) lloc[rb] += __shfl_xor(lloc[rb], o, kWave);
+    for (int o = 8; o > 0; o >>= 1) lloc[rb] += lane_xor_f(lloc[rb], o, lane);
   if (col == 0)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) redf[wave][rb * 4 + grp] = lloc[rb];
@@ -859,7 +860,7 @@ __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
     mmax = fmaxf(mmax, ws_l[s]);
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, o, kWave));
+  for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, lane_xor_f(mmax, o, lane));
   if (lane == 0) red[wave] = mmax;
   __syncthreads();
   float M = red[0];
@@ -874,7 +875,7 @@ __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
     ws_l[s] = w;
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o, kWave);
+  for (int o = 32; o > 0; o >>= 1) lsum += lane_xor_f(lsum, o, lane);
   if (lane == 0) red[wave] = lsum;
   __syncthreads();
   float l = 0.0f;

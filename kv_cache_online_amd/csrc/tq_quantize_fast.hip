@@ -148,26 +148,6 @@ __device__ inline uint32_t wlane(uint32_t v, int lane, uint32_t old) {
   return static_cast<uint32_t>(tq_writelane_i32(static_cast<int>(v), lane, static_cast<int>(old)));
 }
 
-// The value of lane l ^ s (s = 16, 8, 4, 2, 1).  Below 16 the exchange stays
-// inside a 16-lane row, so it is a DPP move (no LDS round trip): a rotation by
-// 8, quad permutations for 2 and 1, and for 4 a shift up or down by 4 chosen
-// by the lane's own bit 2 (DPP controls as measured on gfx950: row_shl:n reads
-// lane l + n, row_shr:n lane l - n, row_ror:8 lane l ^ 8).
-__device__ inline uint32_t lane_xor(uint32_t a, int s, int lane) {
-  const int v = static_cast<int>(a);
-  switch (s) {
-    case 8: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
-    case 4: {
-      const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);
-      const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
-      return static_cast<uint32_t>((lane & 4) ? dn : up);
-    }
-    case 2: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
-    case 1: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
-    default: return static_cast<uint32_t>(__shfl_xor(v, s, kWave));
-  }
-}
-
 // Sum of v over the lanes of an aligned group of 2^k lanes (k <= 3), in every
 // lane of the group, by DPP exchanges (lane_xor).
 template <int K>
