@@ -147,8 +147,8 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    ss += __shfl_xor(ss, o, kWave);
-    smax = fmaxf(smax, __shfl_xor(smax, o, kWave));
+    ss += lane_xor_f(ss, o, lane);
+    smax = fmaxf(smax, lane_xor_f(smax, o, lane));
   }
   if (lane == 0) {
     red[0][wave] = ss;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq
     q[h][j] = bh < nq ? load_q(a.q, a.dtype, size_t(bh) * D + j) : 0.0f;
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) smax = fmaxf(smax, __shfl_xor(smax, o, kWave));
+  for (int o = 32; o > 0; o >>= 1) smax = fmaxf(smax, lane_xor_f(smax, o, lane));
   if (lane == 0) red[wave] = smax;
   __syncthreads();
   // ||q|| of heads HG / 4 wave ..
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq
     float ss = 0.0f;
     for (int j = lane; j < D; j += 64) ss = fmaf(q[h][j], q[h][j], ss);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+    for (int o = 32; o > 0; o >>= 1) ss += lane_xor_f(ss, o, lane);
     if (lane == 0) qn[h] = sqrtf(ss);
   }
 #pragma unroll
