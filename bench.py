@@ -123,6 +123,48 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_byt
     print(json.dumps(out, indent=1))
 
 
+def quality_vs_unquantized(w, Kn, Vn, Qn, out):
+    """The decode output against softmax attention over the unquantized K, V and q
+    (float64 on the host, scale 1/sqrt(d)): relative L2 error and cosine per query
+    head.  Reported, not pass/fail."""
+    import workloads as W
+    G = w.n_q_heads // w.n_kv_heads
+    scale = 1.0 / math.sqrt(w.d)
+    rel, cos = [], []
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            k = W.to_f64(Kn[b, h], w.dtype)
+            v = W.to_f64(Vn[b, h], w.dtype)
+            q = W.to_f64(Qn[b, h * G:(h + 1) * G], w.dtype)
+            sc = (q @ k.T) * scale
+            sc -= sc.max(axis=1, keepdims=True)
+            pr = np.exp(sc)
+            ref = (pr @ v) / pr.sum(axis=1, keepdims=True)
+            got = out[b, h * G:(h + 1) * G].astype(np.float64)
+            rel.extend(np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1))
+            cos.extend(np.sum(got * ref, axis=1) / (np.linalg.norm(got, axis=1) * np.linalg.norm(ref, axis=1)))
+    return {"reference": "softmax attention over the unquantized K, V, q (float64, host)",
+            "query_heads": len(rel), "rel_l2_mean": float(np.mean(rel)), "rel_l2_max": float(np.max(rel)),
+            "cosine_min": float(np.min(cos))}
+
+
+def quality_report(w, s, rot, proj, K0, V0, Q, st_d, ln_d, max_len, cap, dst, Kn, Vn, Qn, out):
+    """quality_vs_unquantized for the workload's preset and, beside it, for the
+    same index bits with the residual sketch off (MSE-only): the sketch makes the
+    inner products unbiased at the price of variance, which the softmax
+    amplifies where the scores are spread (outlier channels)."""
+    from kv_cache_online_amd.session import TQSession
+    rep = {"preset": quality_vs_unquantized(w, Kn, Vn, Qn, out)}
+    if w.sketch:
+        s2 = TQSession(w.d, w.n_kv_heads, w.n_q_heads, rot, proj, k_bits=w.bits_mse, v_bits=w.bits_mse,
+                       k_sketch=0, v_sketch=0)
+        kc, vc = s2.new_caches(cap)
+        s2.quantize(K0, V0, dst, kc, vc)
+        out2 = s2.decode(Q, st_d, ln_d, max_len, kc, vc)
+        rep[f"mse_only_{w.bits_mse}bit"] = quality_vs_unquantized(w, Kn, Vn, Qn, out2.cpu().numpy())
+    return rep
+
+
 def cpu_baseline(w, rot, proj, seconds):
     """Time the oracle (float64 NumPy) on a bounded sample of the same workload."""
     import oracle as O
@@ -224,10 +266,11 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
         return t.view(torch.bfloat16) if a.dtype == np.uint16 else t
 
-    K0, V0 = dev(W.kv_batch(w, 0)), dev(W.kv_batch(w, 1))
+    Kn, Vn, Qn = W.kv_batch(w, 0), W.kv_batch(w, 1), W.queries(w)
+    K0, V0 = dev(Kn), dev(Vn)
     Ks, Vs = [K0] + [K0.clone() for _ in range(R - 1)], [V0] + [V0.clone() for _ in range(R - 1)]
     caches = [s.new_caches(cap) for _ in range(R)]
-    Q = dev(W.queries(w))
+    Q = dev(Qn)
     dst = torch.from_numpy(starts).cuda()
     st_d = torch.from_numpy(starts).cuda()
     ln_d = torch.from_numpy(lens.astype(np.int32)).cuda()
@@ -310,6 +353,8 @@ def main():
                    "accumulate, fp32/fp64 softmax and merge",
         "roofline": dominant, "roofline_decode": roof_dec, "roofline_quantize": roof_q,
         "source_hash": source_hash(),
+        "quality": quality_report(w, s, rot, proj, K0, V0, Q, st_d, ln_d, max_len, cap, dst, Kn, Vn, Qn,
+                                  out.cpu().numpy()),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, rot, proj, args.cpu_seconds)
