@@ -230,6 +230,21 @@ def test_mse_only_and_asymmetric_bits(wid):
         check_decode(run, run.decode(), label=f"k{kb}s{ks}-v{vb}s{vs}")
 
 
+@pytest.mark.parametrize("wid", [2, 5])
+@pytest.mark.parametrize("bits", [1, 2, 3])
+@pytest.mark.parametrize("sketch", [0, 1])
+def test_bits_matrix(wid, bits, sketch):
+    """Every index width with and without the sign sketch, at d = 128 and d = 256
+    (each a distinct kernel instantiation), on a short ragged context."""
+    w = W.WORKLOADS[wid]
+    run = Run(w, batch=1, n_tokens=229, k_bits=bits, v_bits=bits, k_sketch=sketch, v_sketch=sketch)
+    _log(f"workload {wid}: b' = {bits}, sketch {sketch}")
+    dbg = run.quantize()
+    check_quantize(run, dbg, label=f"w{wid}-b{bits}-s{sketch}")
+    check_decode(run, run.decode(), label=f"w{wid}-b{bits}-s{sketch}")
+    assert run.status() == 0
+
+
 def test_fp32_input_d256():
     """fp32 K/V at d = 256: the reference-grade quantize (the matrix-core one takes bf16 there)."""
     w = W.small(W.WORKLOADS[5], dtype="f32")
