@@ -205,6 +205,25 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
                         const tq_cache *kc, const tq_cache *vc, float sm_scale, float *out,
                         uint32_t *status, void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes tq_score_keys needs for n_q queries over at most max_n keys. */
+size_t tq_score_workspace_bytes(const tq_config *cfg, int32_t n_q, int32_t max_n);
+
+/* Inner-product scores of n_q queries against packed keys: the compressed
+ * vectors as a search index (ast-softpro.ru, "Технология TurboQuant и её
+ * применение с локальными LLM", section 6.4 and FAQ: vector search in RAG
+ * systems).  scores[j][i] = <q_j, k~_i> for the key in slot start + i of head
+ * kv_head of kc, i < n, where k~ is the vector the record encodes
+ * (nu~ Pi^T c[idx] + sqrt(pi/2)/m rho~ S^T sgn, section 1.2) -- the estimator
+ * decode attention scores, without a softmax scale.  q: device
+ * [n_q][d] in dtype dt, n_q a positive multiple of 8; kc: TOKEN_MAJOR.
+ * scores: device fp32 [n_q][n] (row stride n).  A range past the capacity
+ * is rejected (TQ_ERR_INVALID_ARG); d other than 128 or 256 and an
+ * asymmetric codebook give TQ_ERR_UNSUPPORTED.  workspace: device,
+ * >= tq_score_workspace_bytes.  Enqueues on stream and returns. */
+int tq_score_keys(const tq_config *cfg, const void *q, tq_dtype dt, int32_t n_q, const tq_cache *kc,
+                  int32_t kv_head, int64_t start, int32_t n, float *scores, uint32_t *status,
+                  void *workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Static string for a tq_status value. */
 const char *tq_status_string(int status);
 

@@ -24,7 +24,8 @@ TQ_FLAG_NONFINITE_INPUT, TQ_FLAG_SCALE_OVERFLOW, TQ_FLAG_OUT_OF_RANGE = 1, 2, 4
 TQ_MAX_LEVELS = 8
 
 EXPORTED = ("tq_build_codebook", "tq_build_codebook_sphere", "tq_prepare_bytes", "tq_prepare", "tq_quantize_kv",
-            "tq_decode_workspace_bytes", "tq_decode_attention", "tq_status_string")
+            "tq_decode_workspace_bytes", "tq_decode_attention", "tq_score_workspace_bytes", "tq_score_keys",
+            "tq_status_string")
 
 
 class tq_codebook(Structure):
@@ -79,6 +80,11 @@ def _load():
                                         c_void_p, c_int32, POINTER(tq_cache), POINTER(tq_cache),
                                         c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.tq_decode_attention.restype = c_int
+    lib.tq_score_workspace_bytes.argtypes = [POINTER(tq_config), c_int32, c_int32]
+    lib.tq_score_workspace_bytes.restype = c_size_t
+    lib.tq_score_keys.argtypes = [POINTER(tq_config), c_void_p, c_int, c_int32, POINTER(tq_cache), c_int32,
+                                  ctypes.c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.tq_score_keys.restype = c_int
     lib.tq_status_string.argtypes = [c_int]
     lib.tq_status_string.restype = c_char_p
     return lib
@@ -160,6 +166,18 @@ def tq_decode_attention(cfg: tq_config, q, dt: int, batch: int, seq_start, seq_l
                                  _ptr(status), _ptr(workspace), ws_bytes, _stream(stream))
     if st != TQ_OK:
         raise TQError(st, "tq_decode_attention")
+
+
+def tq_score_workspace_bytes(cfg: tq_config, n_q: int, max_n: int) -> int:
+    return LIB.tq_score_workspace_bytes(ctypes.byref(cfg), n_q, max_n)
+
+
+def tq_score_keys(cfg: tq_config, q, dt: int, n_q: int, kc: tq_cache, kv_head: int, start: int, n: int,
+                  scores, status, workspace, ws_bytes: int, stream=None) -> None:
+    st = LIB.tq_score_keys(ctypes.byref(cfg), _ptr(q), dt, n_q, ctypes.byref(kc), kv_head, start, n,
+                           _ptr(scores), _ptr(status), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != TQ_OK:
+        raise TQError(st, "tq_score_keys")
 
 
 # ------------------------------------------------- struct helpers (host) ---

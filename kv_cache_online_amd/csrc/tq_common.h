@@ -118,6 +118,15 @@ struct DecodeArgs {
   int32_t split_tokens, n_split;
   float *out;            // [batch][Hq][d]
   uint32_t *status;
+  double qbase;          // scale of the score digit sums before 2^-E: sm_scale log2(e) (decode), 1 (scores)
+  // key scoring (tq_score_keys): every block reads key head kv_fixed (-1: its own),
+  // slots [fix_start, fix_start + fix_len) when seq_start is null, and writes raw
+  // scores [Hq][score_ld] instead of attention partials
+  int32_t kv_fixed;
+  int64_t fix_start;
+  int32_t fix_len;
+  float *scores;
+  int64_t score_ld;
 };
 
 // Host launchers (defined in the .hip translation units).  Return hipError_t.
@@ -125,5 +134,6 @@ int launch_quantize(int d, const QuantArgs &a, hipStream_t s);
 int launch_quantize_fast(int d, const QuantArgs &a, hipStream_t s);
 int launch_decode(int d, const DecodeArgs &a, hipStream_t s);
 int launch_decode_fast(int d, int rb, const DecodeArgs &a, hipStream_t s);
+int launch_score_fast(int d, const DecodeArgs &a, hipStream_t s);
 
 }  // namespace tq

@@ -95,8 +95,9 @@ __device__ inline uint32_t digits(int32_t f) { return static_cast<uint32_t>(f + 
 __device__ inline int fix_exp(double vmax) { return vmax > 0.0 ? 29 - ilogb(vmax) : 0; }
 
 __device__ inline void clip_seq(const DecodeArgs &a, int b, int64_t *start, int64_t *len) {
-  int64_t s = a.seq_start[b], n = a.seq_len[b];
-  const int64_t cap = a.k.cap < a.v.cap ? a.k.cap : a.v.cap;
+  const bool fixed = a.seq_start == nullptr;  // key scoring: one slot range, keys only
+  int64_t s = fixed ? a.fix_start : a.seq_start[b], n = fixed ? a.fix_len : a.seq_len[b];
+  const int64_t cap = fixed ? a.k.cap : a.k.cap < a.v.cap ? a.k.cap : a.v.cap;
   bool bad = false;
   if (n < 0) { n = 0; bad = true; }
   if (s < 0 || s > cap) { s = 0; n = 0; bad = true; }
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   }
   if (tid == 0 && (t == 0 || t == D / 64)) {
     // alpha (Walsh planes) or beta (sign plane, 0 without one): the scale of the digit sums
-    const double base = double(a.sm_scale) * 1.4426950408889634;  // log2(e): scores in base 2
+    const double base = a.qbase;  // sm_scale log2(e) (scores in base 2), or 1 for raw scores
     int32_t *qc = a.qconst + size_t(bh) * 8;
     if (sgn) qc[5] = __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), -E)));
     else qc[4] = __float_as_int(static_cast<float>(ldexp(base, -E)));
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq
     const int bh = grp * HG + tid;
     if (bh < nq) {
       const int E = fix_exp(scale * double(qn[tid]) * (1.0 + 0x1p-10));
-      const double base = double(a.sm_scale) * 1.4426950408889634;  // log2(e): scores in base 2
+      const double base = a.qbase;  // sm_scale log2(e) (scores in base 2), or 1 for raw scores
       int32_t *qc = a.qconst + size_t(bh) * 8;
       if (sgn) qc[5] = __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), -E)));
       else qc[4] = __float_as_int(static_cast<float>(ldexp(base, -E)));
@@ -403,7 +404,9 @@ struct SplitShape {
   static constexpr int AWP = DEEP ? 2 : 1;
 };
 
-template <int D, int RB, int BQK, int BQV, bool DEEP>
+// SCORES: key scoring (tq_score_keys) -- phase 1 only, over key head a.kv_fixed,
+// writing each score instead of the split's attention partial.
+template <int D, int RB, int BQK, int BQV, bool DEEP, bool SCORES = false>
 __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   using P = SplitShape<D, RB, BQK, BQV, DEEP>;
   constexpr int C = P::C, W = P::W, NB = P::NB, NW = P::NW, G = P::G, PK = P::PK, PV = P::PV;
@@ -433,7 +436,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   const int bh0 = b * a.Hq + h * G;
   const int stride = 2 + 2 * D;
   if (lo >= hi) {
-    if (tid < G) {
+    if (!SCORES && tid < G) {
       float *o = a.part + (size_t(bh0 + tid) * a.n_split + split) * stride;
       o[0] = -INFINITY;
       o[1] = 0.0f;
@@ -448,17 +451,19 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   const int kslots = static_cast<int>((kcap - abase) < S ? (kcap - abase) : S);
   const int64_t blk0 = abase >> 5;
   const int vblk = static_cast<int>((vblocks - blk0) < (S >> 5) ? (vblocks - blk0) : (S >> 5));
-  const u4 rk = make_rsrc(a.k.idx + (int64_t(h) * kcap + abase) * BQK * W, kslots * KREC);
-  const u4 rks = make_rsrc(skk ? a.k.sgn + (int64_t(h) * kcap + abase) * W : a.k.idx, skk ? kslots * KSREC : 0);
-  const u4 rkc = make_rsrc(a.k.scl + (int64_t(h) * kcap + abase) * 2, kslots * 4);
+  const int hk = SCORES ? a.kv_fixed : h;  // key head
+  const u4 rk = make_rsrc(a.k.idx + (int64_t(hk) * kcap + abase) * BQK * W, kslots * KREC);
+  const u4 rks = make_rsrc(skk ? a.k.sgn + (int64_t(hk) * kcap + abase) * W : a.k.idx, skk ? kslots * KSREC : 0);
+  const u4 rkc = make_rsrc(a.k.scl + (int64_t(hk) * kcap + abase) * 2, kslots * 4);
   const int vslots = static_cast<int>((vcap - abase) < S ? (vcap - abase) : S);
-  const u4 rvc = make_rsrc(a.v.scl + (int64_t(h) * vcap + abase) * 2, vslots * 4);
-  const u4 rv = make_rsrc(a.v.idx + (int64_t(h) * vblocks + blk0) * BQV * D, vblk * VREC);
-  const u4 rvs = make_rsrc(skv ? a.v.sgn + (int64_t(h) * vblocks + blk0) * D : a.v.idx, skv ? vblk * VSREC : 0);
+  // (scoring has no value cache: empty descriptors, whose loads return zeros)
+  const u4 rvc = SCORES ? make_rsrc(a.k.scl, 0) : make_rsrc(a.v.scl + (int64_t(h) * vcap + abase) * 2, vslots * 4);
+  const u4 rv = SCORES ? make_rsrc(a.k.idx, 0) : make_rsrc(a.v.idx + (int64_t(h) * vblocks + blk0) * BQV * D, vblk * VREC);
+  const u4 rvs = SCORES || !skv ? make_rsrc(a.k.idx, 0) : make_rsrc(a.v.sgn + (int64_t(h) * vblocks + blk0) * D, vblk * VSREC);
 
   // ---- the wave's chunk stream ----
   const int nk = ntile > wave ? (ntile - wave + 3) >> 2 : 0;  // key tiles of this wave
-  const int nr = (ntile + 3) >> 2;                             // value rounds
+  const int nr = SCORES ? 0 : (ntile + 3) >> 2;               // value rounds
   const int nch = nk + nr;
   // value chunk lane roles: lane -> (block, 16-byte piece) of the wave's coordinates
   const int vblkl = NW == 1 ? (lane >> 3) : (lane >> 4), vpiece = NW == 1 ? (lane & 7) : (lane & 15);
@@ -604,6 +609,22 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
         }
       }
     }
+  }
+  if (SCORES) {
+    // every load this wave issued has landed before it ends (the ring is LDS)
+    wait_vm<0>();
+#pragma unroll
+    for (int kt = 0; kt < kMaxT; ++kt)
+      if (kt < nk)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int t = (wave + 4 * kt) * 64 + nb * 16 + col;
+          if (t >= vlo && t < vhi)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              a.scores[size_t(bh0 + rb * 4 + grp) * a.score_ld + (abase + t - start)] = sreg[kt][nb][rb];
+        }
+    return;
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -1076,7 +1097,36 @@ int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
   return 0;
 }
 
+template <int D, int BQK, bool DEEP>
+int launch_score_bq(const DecodeArgs &a, hipStream_t s) {
+  const dim3 grid(a.n_split, a.Hkv, a.batch);
+  if (a.split_tokens > kMaxT * 256) return 1;
+  hipLaunchKernelGGL((decode_partial_fast<D, 2, BQK, BQK, DEEP, true>), grid, dim3(256), 0, s, a);
+  return 0;
+}
+
+template <int D>
+int launch_score_d(const DecodeArgs &a, hipStream_t s) {
+  const unsigned nq = static_cast<unsigned>(a.batch * a.Hq);
+  if (nq >= 512)
+    hipLaunchKernelGGL(decode_qprep_grouped<D>, dim3((nq + 7) / 8 * (2 * D / 64)), dim3(256), 0, s, a, int(nq));
+  else hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
+  const bool deep = int64_t(a.n_split) * a.Hkv * a.batch <= 1024;
+  switch (a.k.bq) {
+    case 1: return deep ? launch_score_bq<D, 1, true>(a, s) : launch_score_bq<D, 1, false>(a, s);
+    case 2: return deep ? launch_score_bq<D, 2, true>(a, s) : launch_score_bq<D, 2, false>(a, s);
+    case 3: return deep ? launch_score_bq<D, 3, true>(a, s) : launch_score_bq<D, 3, false>(a, s);
+    default: return 1;
+  }
+}
+
 }  // namespace
+
+int launch_score_fast(int d, const DecodeArgs &a, hipStream_t s) {
+  int e = d == 128 ? launch_score_d<128>(a, s) : d == 256 ? launch_score_d<256>(a, s) : 1;
+  if (e) return e;
+  return hipGetLastError() != hipSuccess;
+}
 
 int launch_decode_fast(int d, int rb, const DecodeArgs &a, hipStream_t s) {
   int e = 1;

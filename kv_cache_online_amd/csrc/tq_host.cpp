@@ -477,6 +477,8 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
   a.seq_start = seq_start;
   a.seq_len = seq_len;
   a.sm_scale = sm_scale > 0 ? sm_scale : static_cast<float>(1.0 / std::sqrt(double(cfg->d)));
+  a.qbase = double(a.sm_scale) * 1.4426950408889634;  // log2(e): scores in base 2
+  a.kv_fixed = -1;
   a.kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / cfg->m);
   a.rot = cfg->rot;
   a.proj = cfg->proj;
@@ -500,8 +502,108 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
   }
   a.out = out;
   a.status = status;
-  const int rc = p.fast ? tq::launch_decode_fast(cfg->d, p.rb, a, stream) : tq::launch_decode(cfg->d, a, stream);
+  // the matrix-core decode expands the codebook over odd Walsh terms only, which
+  // holds for an antisymmetric codebook (every Lloyd-Max codebook of a symmetric law)
+  const bool fast = p.fast && cb_symmetric(a.k.cb) && cb_symmetric(a.v.cb);
+  const int rc = fast ? tq::launch_decode_fast(cfg->d, p.rb, a, stream) : tq::launch_decode(cfg->d, a, stream);
   if (rc != 0) return TQ_ERR_LAUNCH;
+  return TQ_OK;
+}
+
+namespace {
+
+// Workspace of tq_score_keys: the query operands and constants of n_q queries
+// taken as n_q / 8 groups of 8 (one group per split-pass block row).
+struct ScorePlan {
+  int32_t split_tokens, n_split;
+  size_t off_qop, off_qconst, total;
+};
+
+ScorePlan score_plan(const tq_config &cfg, int32_t n_q, int32_t max_n) {
+  ScorePlan p{};
+  const int64_t groups = n_q / 8;
+  int64_t st = groups > 0 ? (int64_t(max_n) * groups + 511) / 512 : 256;  // about 512 work-groups
+  st = (st + 255) / 256 * 256;
+  if (st > 1024) st = 1024;
+  if (st < 256) st = 256;
+  p.split_tokens = static_cast<int32_t>(st);
+  p.n_split = static_cast<int32_t>((int64_t(max_n) + 63 + st - 1) / st);
+  if (p.n_split < 1) p.n_split = 1;
+  size_t o = 0;
+  p.off_qop = o;    o = tq::align256(o + size_t(groups) * 2 * 5 * (cfg.d / 64) * 64 * 16);
+  p.off_qconst = o; o = tq::align256(o + size_t(n_q) * 4 * 8);
+  p.total = o;
+  return p;
+}
+
+}  // namespace
+
+size_t tq_score_workspace_bytes(const tq_config *cfg, int32_t n_q, int32_t max_n) {
+  if (!cfg || n_q <= 0 || n_q % 8 || max_n < 0 || cfg->d <= 0) return 0;
+  return score_plan(*cfg, n_q, max_n).total;
+}
+
+int tq_score_keys(const tq_config *cfg, const void *q, tq_dtype dt, int32_t n_q, const tq_cache *kc,
+                  int32_t kv_head, int64_t start, int32_t n, float *scores, uint32_t *status,
+                  void *workspace, size_t ws_bytes, hipStream_t stream) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (dt != TQ_F32 && dt != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (n_q <= 0 || n_q % 8 || n < 0 || start < 0) return TQ_ERR_INVALID_ARG;
+  if (kv_head < 0 || kv_head >= cfg->n_kv_heads) return TQ_ERR_INVALID_ARG;
+  if (n == 0) return TQ_OK;
+  if (!q || !scores || !workspace) return TQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(scores) & 3u))
+    return TQ_ERR_INVALID_ARG;
+  if (status && (reinterpret_cast<uintptr_t>(status) & 3u)) return TQ_ERR_INVALID_ARG;
+  if ((e = check_cache(kc, cfg->k))) return e;
+  if (kc->layout != TQ_LAYOUT_TOKEN_MAJOR) return TQ_ERR_UNSUPPORTED;
+  if (start + n > kc->capacity) return TQ_ERR_INVALID_ARG;
+  if (cfg->d != 128 && cfg->d != 256) return TQ_ERR_UNSUPPORTED;
+  const ScorePlan p = score_plan(*cfg, n_q, n);
+  if (ws_bytes < p.total) return TQ_ERR_WORKSPACE;
+  const tq::PrepLayout L = tq::prep_layout(cfg->d, cfg->m);
+  const auto *prep = static_cast<const unsigned char *>(cfg->prep);
+  auto *ws = static_cast<unsigned char *>(workspace);
+  tq::DecodeArgs a{};
+  a.k.idx = kc->idx;
+  a.k.sgn = kc->sgn;
+  a.k.scl = kc->scl;
+  a.k.cap = kc->capacity;
+  a.k.bq = cfg->k.bits_mse;
+  a.k.sketch = cfg->k.sketch;
+  a.k.cb = cb_f32(cfg->k.cb);
+  if (!cb_symmetric(a.k.cb)) return TQ_ERR_UNSUPPORTED;
+  const tq_codebook &cb = cfg->k.cb;
+  a.walsh_k[0] = cb.walsh[1];
+  a.walsh_k[1] = cb.levels > 2 ? cb.walsh[2] : 0.0;
+  a.walsh_k[2] = cb.levels > 4 ? cb.walsh[4] : 0.0;
+  a.walsh_k[3] = cb.levels > 4 ? cb.walsh[7] : 0.0;
+  a.q = q;
+  a.dtype = dt;
+  a.batch = 1;
+  a.Hq = n_q;
+  a.G = 8;
+  a.Hkv = n_q / 8;  // query groups; every one reads key head kv_head
+  a.kv_fixed = kv_head;
+  a.seq_start = nullptr;
+  a.seq_len = nullptr;
+  a.fix_start = start;
+  a.fix_len = n;
+  a.sm_scale = 1.0f;
+  a.qbase = 1.0;  // raw inner products
+  a.kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / cfg->m);
+  a.rotT = reinterpret_cast<const float *>(prep + L.rotT);
+  a.projT = reinterpret_cast<const float *>(prep + L.projT);
+  a.stnorm = reinterpret_cast<const float *>(prep + L.stnorm);
+  a.split_tokens = p.split_tokens;
+  a.n_split = p.n_split;
+  a.qop = ws + p.off_qop;
+  a.qconst = reinterpret_cast<int32_t *>(ws + p.off_qconst);
+  a.scores = scores;
+  a.score_ld = n;
+  a.status = status;
+  if (tq::launch_score_fast(cfg->d, a, stream) != 0) return TQ_ERR_LAUNCH;
   return TQ_OK;
 }
 

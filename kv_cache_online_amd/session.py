@@ -114,3 +114,18 @@ class TQSession:
                               kc.desc, vc.desc, sm_scale, out, self.status, workspace,
                               workspace.numel(), stream)
         return out
+
+    def score_keys(self, q, kc: PackedCache, kv_head: int, start: int, n: int, out=None, workspace=None,
+                   stream=None):
+        """Inner products of q [n_q][d] (n_q a multiple of 8) with the packed keys in
+        slots [start, start + n) of kv head kv_head: fp32 [n_q][n]."""
+        n_q, d = q.shape
+        assert d == self.d and q.is_contiguous()
+        if out is None:
+            out = torch.empty(n_q, n, dtype=torch.float32, device=self.device)
+        if workspace is None:
+            nb = B.tq_score_workspace_bytes(self.cfg, n_q, n)
+            workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+        B.tq_score_keys(self.cfg, q, self.dtype_code(q), n_q, kc.desc, kv_head, start, n, out, self.status,
+                        workspace, workspace.numel(), stream)
+        return out

@@ -30,7 +30,7 @@ the original space with the stored fp16 norm; S is m x d with N(0,1) entries
 and m = d; sign(0) counts as +; the residual is reconstructed as
 sqrt(pi/2)/m * ||r|| * S^T sign(S r) (the scaling that makes the inner-product
 estimate unbiased); attention is softmax(q k^T / sqrt(d)) V with query head h
-reading kv head h // G.
+reading kv head h // G; a search score is <q, x_hat>.
 
 Parity status: every function here is pinned by tests in ``tests/test_oracle_*``
 against closed forms, brute force, numerical integration or library routines.
@@ -42,7 +42,8 @@ from .layout import (pack_token_major, unpack_token_major, pack_block32,
                      unpack_block32, record_bytes)
 from .dequant import dequantize
 from .attention import attention
+from .search import score_keys
 
 __all__ = ["build_codebook", "build_codebook_sphere", "fp16_round", "quantize", "quantize_conditional",
            "pack_token_major", "unpack_token_major", "pack_block32", "unpack_block32",
-           "record_bytes", "dequantize", "attention"]
+           "record_bytes", "dequantize", "attention", "score_keys"]

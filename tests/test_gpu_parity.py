@@ -245,6 +245,38 @@ def test_bits_matrix(wid, bits, sketch):
     assert run.status() == 0
 
 
+@pytest.mark.parametrize("wid,n_q,off,n", [(2, 8, 37, 1000), (2, 16, 0, 513), (3, 64, 5, 2000), (5, 8, 70, 700),
+                                          (5, 24, 0, 64), (1, 8, 1, 1)])
+def test_score_keys(wid, n_q, off, n):
+    """Search scores of n_q queries against the packed keys of one kv head (slots
+    start + off .. + n), compared per entry with the oracle's <q, x_hat> from the
+    bytes the device wrote; tolerance 1e-5 ||q|| (nu~ + 1.25 rho~), the scale of a
+    score (|<Sq, sgn>| <= sqrt(m) ||S q||)."""
+    w = W.WORKLOADS[wid]
+    run = Run(w, batch=1, n_tokens=off + n + 3)
+    run.quantize()
+    kv_head = w.n_kv_heads - 1
+    rng = np.random.default_rng([wid, n_q, n])
+    q32 = rng.standard_normal((n_q, w.d)).astype(np.float32)
+    qs = W.f32_to_bf16_bits(q32) if w.dtype == "bf16" else q32
+    start = int(run.starts[0]) + off
+    _log(f"score keys: workload {wid}, {n_q} queries x {n} keys from slot {start}")
+    got = run.s.score_keys(run.dev(qs), run.kc, kv_head, start, n).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    idx_w, sgn_w, scl = run.host_caches()[0]
+    slots = np.arange(start, start + n)
+    i, sg, nb, rb = PR.unpack_tokens(idx_w, sgn_w, scl, 0, kv_head, slots, run.k_bits)
+    q64 = W.to_f64(qs, w.dtype)
+    nu, rho = PR.f16(nb), PR.f16(rb)
+    ref = O.score_keys(q64, i, sg if run.k_sketch else None, nu, rho if run.k_sketch else None,
+                       run.rot, run.proj, run.cb_k)
+    tol = 1e-5 * np.linalg.norm(q64, axis=1)[:, None] * (nu + 1.25 * rho)[None, :]
+    err = np.abs(got - ref)
+    _log({"label": f"score w{wid}", "worst_err_over_tol": float(np.max(err / np.maximum(tol, 1e-30)))})
+    assert np.all(err <= tol), (np.max(err), np.argmax(err))
+    assert run.status() == 0
+
+
 def test_fp32_input_d256():
     """fp32 K/V at d = 256: the reference-grade quantize (the matrix-core one takes bf16 there)."""
     w = W.small(W.WORKLOADS[5], dtype="f32")
