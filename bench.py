@@ -214,6 +214,104 @@ def cpu_baseline(w, rot, proj, seconds):
             "quantize_tokens_per_s": n_pos / tq}
 
 
+def search_cpu_baseline(w, rot, proj, Qn, n_q, seconds):
+    """Time the oracle's search scores (unpack + float64 dequantize + q @ k^T) on a
+    bounded sample of keys."""
+    import oracle as O
+    import workloads as W
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max([i.get("num_threads", 0) for i in blas] + [1])
+    except Exception:
+        pass
+    cb = O.build_codebook(w.bits_mse, 1 / math.sqrt(w.d))
+    n = 65536
+    K = W.to_f64(W.kv_chunk(w, 0, 0, 0, n_tokens=n), w.dtype)
+    qk = O.quantize(K, rot, proj, cb)
+    kp = O.pack_token_major(qk["idx"], qk["sgn"], qk["nu_bits"], qk["rho_bits"], w.bits_mse)
+    q = W.to_f64(Qn[0, :n_q], w.dtype)
+    f16 = lambda b: np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
+    reps, t = 0, 0.0
+    while reps < 1 or (t < seconds and reps < 40):
+        t0 = time.perf_counter()
+        i, sg, nb, rb = O.unpack_token_major(*kp, w.bits_mse)
+        O.score_keys(q, i, sg, f16(nb), f16(rb), rot, proj, cb)
+        t += time.perf_counter() - t0
+        reps += 1
+    rec = O.record_bytes(w.d, w.m, w.bits_mse, w.sketch)
+    return {"value": reps * n * (rec + 4 * n_q) / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} packed keys x {n_q} queries: unpack + float64 dequantize + scores, {reps} reps, "
+                      f"{t:.1f} s"}
+
+
+def bench_search(args):
+    """Inner-product search over packed keys (tq_score_keys): a 2^23-vector key
+    index (the keys of the default workload, repeated), scored by n_q queries per
+    call for each n_q of --search-nq (default 8 and 32).  Algorithmic bytes per call: the packed keys read once plus
+    the fp32 scores written."""
+    import torch
+    import workloads as W
+    from kv_cache_online_amd.session import TQSession
+
+    w = W.WORKLOADS[2]
+    rot, proj = W.rotation(w.d, w.wid), W.sketch(w.m, w.d, w.wid)
+    s = TQSession(w.d, 1, 8, rot, proj, k_bits=w.bits_mse, v_bits=w.bits_mse, k_sketch=w.sketch,
+                  v_sketch=w.sketch)
+    Kn, Qn = W.kv_batch(w, 0), W.queries(w)
+    base = w.n_kv_heads * w.seq_len                       # 2^18 key vectors
+    N = 1 << 23
+    K = torch.from_numpy(np.ascontiguousarray(Kn)).cuda().view(torch.bfloat16).reshape(1, 1, base, w.d)
+    kc = s.new_caches(N)[0]
+    for c in range(N // base):
+        s.quantize(K, None, torch.tensor([c * base], dtype=torch.int64, device="cuda"), kc, None)
+    del K
+    stream = torch.cuda.current_stream()
+    rec = packed_record_bytes(w.d, w.m, w.bits_mse, w.sketch)
+    Q = torch.from_numpy(np.ascontiguousarray(Qn)).cuda().view(torch.bfloat16).reshape(-1, w.d)
+    runs = []
+    for n_q in args.search_nq:
+        q = Q[:n_q].contiguous()
+        out = torch.empty(n_q, N, dtype=torch.float32, device="cuda")
+        ws = s.score_workspace(n_q, N)
+        for _ in range(args.warmup):
+            s.score_keys(q, kc, 0, 0, N, out=out, workspace=ws, stream=stream)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            s.score_keys(q, kc, 0, 0, N, out=out, workspace=ws, stream=stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+        assert torch.isfinite(out).all(), "scores not finite"
+        nbytes = N * rec + n_q * N * 4 + n_q * w.d * 2
+        gbs = nbytes / t / 1e9
+        runs.append({"n_q": n_q, "avg_call_s": t, "bytes_per_call": nbytes, "GBps": gbs,
+                     "frac": gbs / HBM_PEAK_GBS, "scores_per_s": n_q * N / t,
+                     "key_GBps": N * rec / t / 1e9})
+        del out
+    status = int(s.status.item()) & 0xFFFFFFFF
+    assert status == 0, f"device status flags {status:#x}"
+    top = runs[-1]
+    res = {
+        "metric": "packed-key inner-product search GB/s (packed keys read + fp32 scores written)",
+        "value": top["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": top["avg_call_s"] * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16+i8", "data": "synthetic (keys of the default workload, repeated)",
+        "config": {"workload": "search-d128-8m-b4", "n_keys": N, "head_dim": w.d, "bits": w.bits, "n_q": top["n_q"]},
+        "roofline": {"bound": "hbm", "achieved": top["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": top["frac"], "traffic": None,
+                     "kernel": "tq_score_keys call: query prep + split scoring", "bytes_per_launch": top["bytes_per_call"],
+                     "avg_launch_s": top["avg_call_s"]},
+        "runs": runs, "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = search_cpu_baseline(w, rot, proj, Qn, top["n_q"], args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +325,10 @@ def main():
                     help="run only plain 1 GiB device copies (HBM counter calibration)")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json from rocprofv3 counter CSVs (no GPU)")
+    ap.add_argument("--search", action="store_true",
+                    help="measure inner-product search over a packed key index instead")
+    ap.add_argument("--search-nq", type=lambda v: [int(x) for x in v.split(",")], default=[8, 32],
+                    help="query counts of the search measurement (multiples of 8; the last one is the headline)")
     args = ap.parse_args()
     if args.traffic:
         import workloads as W
@@ -246,6 +348,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         copy_calibration()
+        return
+    if args.search:
+        bench_search(args)
         return
     w = W.WORKLOADS[args.workload]
     rot, proj = W.rotation(w.d, w.wid), W.sketch(w.m, w.d, w.wid)

@@ -426,7 +426,12 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   // and the LDS base of the direct loads, which must be provably uniform
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 15,
             grp = lane >> 4;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Scoring: every query group reads the same keys, so the groups of one split
+  // run back to back on one XCD (work-groups go round-robin over the 8 XCDs) and
+  // all but the first find the split's keys in that XCD's L2.
+  const int bx = blockIdx.x, b = blockIdx.z;
+  const int split = SCORES ? (bx >> 3) / a.Hkv * 8 + (bx & 7) : bx;
+  const int h = SCORES ? (bx >> 3) % a.Hkv : blockIdx.y;
   int64_t start, len;
   clip_seq(a, b, &start, &len);
   const int S = a.split_tokens;
@@ -1099,7 +1104,9 @@ int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
 
 template <int D, int BQK, bool DEEP>
 int launch_score_bq(const DecodeArgs &a, hipStream_t s) {
-  const dim3 grid(a.n_split, a.Hkv, a.batch);
+  // splits rounded up to a multiple of 8 (the XCD count); the extra work-groups
+  // find an empty range and return
+  const dim3 grid((a.n_split + 7) / 8 * 8 * a.Hkv, 1, a.batch);
   if (a.split_tokens > kMaxT * 256) return 1;
   hipLaunchKernelGGL((decode_partial_fast<D, 2, BQK, BQK, DEEP, true>), grid, dim3(256), 0, s, a);
   return 0;

@@ -115,6 +115,10 @@ class TQSession:
                               workspace.numel(), stream)
         return out
 
+    def score_workspace(self, n_q, max_n):
+        n = B.tq_score_workspace_bytes(self.cfg, n_q, max_n)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+
     def score_keys(self, q, kc: PackedCache, kv_head: int, start: int, n: int, out=None, workspace=None,
                    stream=None):
         """Inner products of q [n_q][d] (n_q a multiple of 8) with the packed keys in
@@ -124,8 +128,7 @@ class TQSession:
         if out is None:
             out = torch.empty(n_q, n, dtype=torch.float32, device=self.device)
         if workspace is None:
-            nb = B.tq_score_workspace_bytes(self.cfg, n_q, n)
-            workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+            workspace = self.score_workspace(n_q, n)
         B.tq_score_keys(self.cfg, q, self.dtype_code(q), n_q, kc.desc, kv_head, start, n, out, self.status,
                         workspace, workspace.numel(), stream)
         return out
