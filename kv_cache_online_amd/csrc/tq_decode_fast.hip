@@ -608,6 +608,12 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
           const float ri = score_sum(acc_i[rb], khi[rb], kli[rb]);
           const float rs = score_sum(acc_s[rb], khs[rb], kls[rb]);
           float sv = fmaf(knu * __int_as_float(qf[rb].x), ri, (krho * __int_as_float(qf[rb].y)) * rs);
+          if (SCORES) {
+            // stored at once (16 consecutive scores per row and lane group); the
+            // ring's waits stay exact, since stores only add to the count behind a chunk
+            if (valid) a.scores[size_t(bh0 + rb * 4 + grp) * a.score_ld + (abase + t - start)] = sv;
+            continue;
+          }
           sv = valid ? sv : -INFINITY;
           sreg[kt][nb][rb] = sv;
           mloc[rb] = fmaxf(mloc[rb], sv);
@@ -618,17 +624,6 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   if (SCORES) {
     // every load this wave issued has landed before it ends (the ring is LDS)
     wait_vm<0>();
-#pragma unroll
-    for (int kt = 0; kt < kMaxT; ++kt)
-      if (kt < nk)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int t = (wave + 4 * kt) * 64 + nb * 16 + col;
-          if (t >= vlo && t < vhi)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              a.scores[size_t(bh0 + rb * 4 + grp) * a.score_ld + (abase + t - start)] = sreg[kt][nb][rb];
-        }
     return;
   }
 #pragma unroll
@@ -1102,13 +1097,13 @@ int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
   return 0;
 }
 
-template <int D, int BQK, bool DEEP>
+template <int D, int RB, int BQK, bool DEEP>
 int launch_score_bq(const DecodeArgs &a, hipStream_t s) {
   // splits rounded up to a multiple of 8 (the XCD count); the extra work-groups
   // find an empty range and return
   const dim3 grid((a.n_split + 7) / 8 * 8 * a.Hkv, 1, a.batch);
   if (a.split_tokens > kMaxT * 256) return 1;
-  hipLaunchKernelGGL((decode_partial_fast<D, 2, BQK, BQK, DEEP, true>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, BQK, DEEP, true>), grid, dim3(256), 0, s, a);
   return 0;
 }
 
@@ -1119,10 +1114,21 @@ int launch_score_d(const DecodeArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(decode_qprep_grouped<D>, dim3((nq + 7) / 8 * (2 * D / 64)), dim3(256), 0, s, a, int(nq));
   else hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
   const bool deep = int64_t(a.n_split) * a.Hkv * a.batch <= 1024;
+  // groups of 16 queries (four row blocks) at d = 128, where their operands fit
+  // in registers: each expansion of a key plane then feeds four MFMAs
+  if constexpr (D == 128) {
+    if (a.G == 16) switch (a.k.bq) {
+      case 1: return deep ? launch_score_bq<D, 4, 1, true>(a, s) : launch_score_bq<D, 4, 1, false>(a, s);
+      case 2: return deep ? launch_score_bq<D, 4, 2, true>(a, s) : launch_score_bq<D, 4, 2, false>(a, s);
+      case 3: return deep ? launch_score_bq<D, 4, 3, true>(a, s) : launch_score_bq<D, 4, 3, false>(a, s);
+      default: return 1;
+    }
+  }
+  if (a.G != 8) return 1;
   switch (a.k.bq) {
-    case 1: return deep ? launch_score_bq<D, 1, true>(a, s) : launch_score_bq<D, 1, false>(a, s);
-    case 2: return deep ? launch_score_bq<D, 2, true>(a, s) : launch_score_bq<D, 2, false>(a, s);
-    case 3: return deep ? launch_score_bq<D, 3, true>(a, s) : launch_score_bq<D, 3, false>(a, s);
+    case 1: return deep ? launch_score_bq<D, 2, 1, true>(a, s) : launch_score_bq<D, 2, 1, false>(a, s);
+    case 2: return deep ? launch_score_bq<D, 2, 2, true>(a, s) : launch_score_bq<D, 2, 2, false>(a, s);
+    case 3: return deep ? launch_score_bq<D, 2, 3, true>(a, s) : launch_score_bq<D, 2, 3, false>(a, s);
     default: return 1;
   }
 }

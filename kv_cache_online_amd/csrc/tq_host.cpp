@@ -512,16 +512,21 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
 
 namespace {
 
+// Queries per split-pass block of tq_score_keys: 16 at d = 128 when n_q allows
+// (four MFMA row blocks, whose operands fit in registers there), else 8.
+int32_t score_group(const tq_config &cfg, int32_t n_q) { return cfg.d == 128 && n_q % 16 == 0 ? 16 : 8; }
+
 // Workspace of tq_score_keys: the query operands and constants of n_q queries
-// taken as n_q / 8 groups of 8 (one group per split-pass block row).
+// (the operand bytes per query do not depend on the group size).
 struct ScorePlan {
-  int32_t split_tokens, n_split;
+  int32_t group, split_tokens, n_split;
   size_t off_qop, off_qconst, total;
 };
 
 ScorePlan score_plan(const tq_config &cfg, int32_t n_q, int32_t max_n) {
   ScorePlan p{};
-  const int64_t groups = n_q / 8;
+  p.group = score_group(cfg, n_q);
+  const int64_t groups = n_q / p.group;
   int64_t st = groups > 0 ? (int64_t(max_n) * groups + 511) / 512 : 256;  // about 512 work-groups
   st = (st + 255) / 256 * 256;
   if (st > 1024) st = 1024;
@@ -530,7 +535,7 @@ ScorePlan score_plan(const tq_config &cfg, int32_t n_q, int32_t max_n) {
   p.n_split = static_cast<int32_t>((int64_t(max_n) + 63 + st - 1) / st);
   if (p.n_split < 1) p.n_split = 1;
   size_t o = 0;
-  p.off_qop = o;    o = tq::align256(o + size_t(groups) * 2 * 5 * (cfg.d / 64) * 64 * 16);
+  p.off_qop = o;    o = tq::align256(o + size_t(n_q / 4) * 5 * (cfg.d / 64) * 64 * 16);
   p.off_qconst = o; o = tq::align256(o + size_t(n_q) * 4 * 8);
   p.total = o;
   return p;
@@ -583,8 +588,8 @@ int tq_score_keys(const tq_config *cfg, const void *q, tq_dtype dt, int32_t n_q,
   a.dtype = dt;
   a.batch = 1;
   a.Hq = n_q;
-  a.G = 8;
-  a.Hkv = n_q / 8;  // query groups; every one reads key head kv_head
+  a.G = p.group;
+  a.Hkv = n_q / p.group;  // query groups; every one reads key head kv_head
   a.kv_fixed = kv_head;
   a.seq_start = nullptr;
   a.seq_len = nullptr;
