@@ -87,6 +87,13 @@ __host__ inline FastDiv make_fastdiv(uint32_t d) {
 
 __device__ inline uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.s; }
 
+// A wave-uniform read of memory that no kernel of this launch writes, through
+// the scalar cache (constant address space): its wait is on the scalar counter,
+// so it does not wait behind the wave's outstanding vector loads and stores.
+__device__ inline int64_t load_uniform(const int64_t *p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) int64_t *>(reinterpret_cast<uintptr_t>(p));
+}
+
 // Tile `tile` of TT vectors: tiles run over (sequence, head, k), and tile k of a
 // sequence starts at the 32-slot boundary at or below its first slot, plus TT k.
 template <int TT>
@@ -96,7 +103,7 @@ __device__ inline Tile tile_at(const QuantArgs &a, uint32_t tile, FastDiv ftpb, 
   const int k = static_cast<int>(tile - bh * ftpb.d);
   T.b = static_cast<int>(fdiv(bh, fh));
   T.h = static_cast<int>(bh - uint32_t(T.b) * fh.d);
-  const int64_t d0 = a.dst[T.b];
+  const int64_t d0 = load_uniform(a.dst + T.b);
   const int sh = static_cast<int>(d0 & 31);
   T.base = (d0 - sh) + TT * int64_t(k);
   T.t0 = TT * k - sh;
