@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, spec
 BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix, spec
 METRIC = "packed-KV decode-attention GB/s (% HBM peak); KV quantize tokens/s"
+SEARCH_WORKLOAD = "search-d128-8m-b4"
 
 
 def source_hash():
@@ -63,9 +64,9 @@ def traffic_for(prefixes, workload):
         t = json.load(open(p))
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != source_hash() or t.get("workload") != workload:
+    if t.get("source_hash") != source_hash() or workload not in t.get("workloads", {}):
         return None
-    ks = t.get("kernels", {})
+    ks = t["workloads"][workload].get("kernels", {})
     total = 0.0
     for pre, n in prefixes:
         hit = [v["bytes"] for k, v in ks.items() if k.startswith(pre)]
@@ -115,9 +116,18 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_byt
         if k in write and k.startswith(("quantize", "decode")):
             kernels[k] = {"fetch_bytes": fetch[k] * f_scale, "write_bytes": write[k] * w_scale,
                           "bytes": fetch[k] * f_scale + write[k] * w_scale}
-    out = {"source_hash": source_hash(), "workload": workload, "copy_kernel": ck, "copy_bytes": copy_bytes,
-           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels}
     path = os.path.join(ROOT, "profiles", "traffic.json")
+    workloads = {}
+    if os.path.exists(path):   # keep the other workloads' entries taken on the same sources
+        try:
+            old = json.load(open(path))
+            if old.get("source_hash") == source_hash():
+                workloads = old.get("workloads", {})
+        except (OSError, ValueError):
+            pass
+    workloads[workload] = {"kernels": kernels}
+    out = {"source_hash": source_hash(), "copy_kernel": ck, "copy_bytes": copy_bytes,
+           "fetch_scale": f_scale, "write_scale": w_scale, "workloads": workloads}
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
@@ -300,9 +310,10 @@ def bench_search(args):
         "value": top["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": top["avg_call_s"] * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16+i8", "data": "synthetic (keys of the default workload, repeated)",
-        "config": {"workload": "search-d128-8m-b4", "n_keys": N, "head_dim": w.d, "bits": w.bits, "n_q": top["n_q"]},
+        "config": {"workload": SEARCH_WORKLOAD, "n_keys": N, "head_dim": w.d, "bits": w.bits, "n_q": top["n_q"]},
         "roofline": {"bound": "hbm", "achieved": top["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": top["frac"], "traffic": None,
+                     "frac": top["frac"],
+                     "traffic": traffic_for([("decode_qprep", 1), ("decode_partial", 1)], SEARCH_WORKLOAD),
                      "kernel": "tq_score_keys call: query prep + split scoring", "bytes_per_launch": top["bytes_per_call"],
                      "avg_launch_s": top["avg_call_s"]},
         "runs": runs, "source_hash": source_hash(),
@@ -332,7 +343,8 @@ def main():
     args = ap.parse_args()
     if args.traffic:
         import workloads as W
-        write_traffic(*args.traffic, copy_bytes=1 << 30, workload=W.WORKLOADS[args.workload].name)
+        write_traffic(*args.traffic, copy_bytes=1 << 30,
+                      workload=SEARCH_WORKLOAD if args.search else W.WORKLOADS[args.workload].name)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
