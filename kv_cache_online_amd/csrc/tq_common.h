@@ -127,6 +127,7 @@ struct DecodeArgs {
   int32_t fix_len;
   float *scores;
   int64_t score_ld;
+  float *score_dummy;  // 64 words that scoring lanes outside the range write instead
 };
 
 // Host launchers (defined in the .hip translation units).  Return hipError_t.

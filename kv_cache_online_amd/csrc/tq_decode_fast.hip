@@ -497,8 +497,21 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
     }
   };
   auto wait_chunk = [&](int s) {
-    if (s + kSlots - 1 < nch) wait_vm<(kSlots - 1) * P::NI_MIN>();
-    else wait_vm<0>();
+    if (s + kSlots - 1 < nch) {
+      if (SCORES) {
+        // Scoring also stores 4 RB scores per lane and tile, unconditionally (one
+        // store instruction each), between the chunk issues; vector loads and
+        // stores complete in issue order, so the stores issued after chunk s --
+        // those of the min(s, kSlots - 1) tiles since -- count behind it too.
+        if (s == 0) wait_vm<(kSlots - 1) * P::NI_MIN>();
+        else if (s == 1 || kSlots == 2) wait_vm<(kSlots - 1) * P::NI_MIN + 4 * RB>();
+        else wait_vm<(kSlots - 1) * P::NI_MIN + 8 * RB>();
+      } else {
+        wait_vm<(kSlots - 1) * P::NI_MIN>();
+      }
+    } else {
+      wait_vm<0>();
+    }
   };
 
   // The first kSlots - 1 chunks, then the query operands and constants as plain
@@ -609,9 +622,12 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
           const float rs = score_sum(acc_s[rb], khs[rb], kls[rb]);
           float sv = fmaf(knu * __int_as_float(qf[rb].x), ri, (krho * __int_as_float(qf[rb].y)) * rs);
           if (SCORES) {
-            // stored at once (16 consecutive scores per row and lane group); the
-            // ring's waits stay exact, since stores only add to the count behind a chunk
-            if (valid) a.scores[size_t(bh0 + rb * 4 + grp) * a.score_ld + (abase + t - start)] = sv;
+            // stored at once (16 consecutive scores per row and lane group), by every
+            // lane: a slot outside the range writes a per-lane dummy word instead, so
+            // that the number of stores per tile is fixed for the ring's waits
+            float *dst = valid ? a.scores + (size_t(bh0 + rb * 4 + grp) * a.score_ld + (abase + t - start))
+                               : a.score_dummy + lane;
+            *dst = sv;
             continue;
           }
           sv = valid ? sv : -INFINITY;

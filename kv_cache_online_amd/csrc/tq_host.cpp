@@ -516,11 +516,12 @@ namespace {
 // (four MFMA row blocks, whose operands fit in registers there), else 8.
 int32_t score_group(const tq_config &cfg, int32_t n_q) { return cfg.d == 128 && n_q % 16 == 0 ? 16 : 8; }
 
-// Workspace of tq_score_keys: the query operands and constants of n_q queries
+// Workspace of tq_score_keys: the query operands and constants of n_q queries,
+// and 64 words that scoring lanes outside the key range write instead
 // (the operand bytes per query do not depend on the group size).
 struct ScorePlan {
   int32_t group, split_tokens, n_split;
-  size_t off_qop, off_qconst, total;
+  size_t off_qop, off_qconst, off_dummy, total;
 };
 
 ScorePlan score_plan(const tq_config &cfg, int32_t n_q, int32_t max_n) {
@@ -537,6 +538,7 @@ ScorePlan score_plan(const tq_config &cfg, int32_t n_q, int32_t max_n) {
   size_t o = 0;
   p.off_qop = o;    o = tq::align256(o + size_t(n_q / 4) * 5 * (cfg.d / 64) * 64 * 16);
   p.off_qconst = o; o = tq::align256(o + size_t(n_q) * 4 * 8);
+  p.off_dummy = o;  o = tq::align256(o + 64 * 4);
   p.total = o;
   return p;
 }
@@ -607,6 +609,7 @@ int tq_score_keys(const tq_config *cfg, const void *q, tq_dtype dt, int32_t n_q,
   a.qconst = reinterpret_cast<int32_t *>(ws + p.off_qconst);
   a.scores = scores;
   a.score_ld = n;
+  a.score_dummy = reinterpret_cast<float *>(ws + p.off_dummy);
   a.status = status;
   if (tq::launch_score_fast(cfg->d, a, stream) != 0) return TQ_ERR_LAUNCH;
   return TQ_OK;
