@@ -222,6 +222,49 @@ def test_decode_validation():
     assert _dec(bad, ws_bytes=1 << 30) == B.TQ_ERR_UNSUPPORTED
 
 
+def _score(cfg, ws_bytes=None, **kw):
+    args = dict(q=FAKE, dt=B.TQ_BF16, n_q=16, kc=_cache(B.TQ_LAYOUT_TOKEN_MAJOR, 8192), kv_head=3, start=100,
+                n=1000, scores=FAKE, ws=FAKE)
+    args.update(kw)
+    need = B.LIB.tq_score_workspace_bytes(ctypes.byref(cfg), args["n_q"], args["n"])
+    return B.LIB.tq_score_keys(ctypes.byref(cfg), args["q"], args["dt"], args["n_q"], ctypes.byref(args["kc"]),
+                               args["kv_head"], args["start"], args["n"], args["scores"], None, args["ws"],
+                               need - 1 if ws_bytes is None else ws_bytes, None)
+
+
+def test_score_validation():
+    """tq_score_keys rejects bad arguments before anything is enqueued."""
+    cfg = _cfg()
+    big = 1 << 30
+    assert _score(cfg) == B.TQ_ERR_WORKSPACE
+    assert _score(cfg, n=0, ws_bytes=big) == B.TQ_OK                     # nothing to score
+    for n_q in (0, 12, -8):                                              # a positive multiple of 8
+        assert _score(cfg, n_q=n_q, ws_bytes=big) == B.TQ_ERR_INVALID_ARG
+    assert _score(cfg, dt=7, ws_bytes=big) == B.TQ_ERR_INVALID_ARG
+    assert _score(cfg, kv_head=8, ws_bytes=big) == B.TQ_ERR_INVALID_ARG  # 8 kv heads
+    assert _score(cfg, kv_head=-1, ws_bytes=big) == B.TQ_ERR_INVALID_ARG
+    assert _score(cfg, start=-1, ws_bytes=big) == B.TQ_ERR_INVALID_ARG
+    assert _score(cfg, start=8000, n=193, ws_bytes=big) == B.TQ_ERR_INVALID_ARG  # past the capacity
+    assert _score(cfg, q=None, ws_bytes=big) == B.TQ_ERR_INVALID_ARG
+    assert _score(cfg, q=FAKE + 4, ws_bytes=big) == B.TQ_ERR_INVALID_ARG  # misaligned
+    assert _score(cfg, scores=FAKE + 2, ws_bytes=big) == B.TQ_ERR_INVALID_ARG
+    assert _score(cfg, kc=_cache(B.TQ_LAYOUT_BLOCK32, 8192), ws_bytes=big) == B.TQ_ERR_UNSUPPORTED
+    assert _score(_cfg(d=64), ws_bytes=big) == B.TQ_ERR_UNSUPPORTED
+    asym = _cfg()
+    c = asym.k.cb
+    for i in range(c.levels):                 # shift the codebook: still ordered, no longer odd
+        c.centroid[i] += 1e-3
+        c.centroid_f32[i] += 1e-3
+    for i in range(c.levels - 1):
+        c.boundary[i] += 1e-3
+        c.boundary_f32[i] += 1e-3
+    assert _score(asym, ws_bytes=big) == B.TQ_ERR_UNSUPPORTED
+    assert B.LIB.tq_score_workspace_bytes(ctypes.byref(cfg), 12, 1000) == 0
+    a = B.LIB.tq_score_workspace_bytes(ctypes.byref(cfg), 8, 1000)
+    b = B.LIB.tq_score_workspace_bytes(ctypes.byref(cfg), 64, 1 << 20)
+    assert 0 < a <= b
+
+
 def test_workspace_plan_monotone():
     cfg = _cfg()
     a = B.tq_decode_workspace_bytes(cfg, 1, 1024)
