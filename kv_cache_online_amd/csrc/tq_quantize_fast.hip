@@ -249,11 +249,13 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
                                                                  32 * kc + 8 * lg)
                             : bf16x8{};
 
-  float tpos[K > 0 ? K : 1], cpos[K + 1];
+  // this lane's coefficient of its vth entry (phase A): upper-half boundary
+  // c16 (c16 < K) or centroid c16 - 4 (4 <= c16 <= 4 + K), else 0
+  float vcoef = 0.0f;
 #pragma unroll
-  for (int k = 0; k < K; ++k) tpos[k] = a.t.cb.thr[L / 2 + k];
+  for (int k = 0; k < K; ++k) vcoef = c16 == k ? a.t.cb.thr[L / 2 + k] : vcoef;
 #pragma unroll
-  for (int k = 0; k <= K; ++k) cpos[k] = a.t.cb.cen[L / 2 + k];
+  for (int k = 0; k <= K; ++k) vcoef = c16 == 4 + k ? a.t.cb.cen[L / 2 + k] : vcoef;
 
   uint32_t flags = 0;
   uint4 xr[NV];
@@ -332,17 +334,14 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
       } else {
         nu = __builtin_amdgcn_sqrtf(ssf);
       }
+      // the eight lanes of row v write one entry of its vth row each (lane c16,
+      // entry c16): ||x|| t_k, or infinity past the K boundaries and for a zero
+      // vector, at 0..3; ||x||~ c_k, or 0 past the K + 1 centroids, at 4..7
+      bool over = false;
+      const uint32_t nb = f16_bits_f32(nu, &over);
+      const float n16 = f16_val(nb);
+      sm.vth[v][c16] = c16 < 4 ? (c16 < K && nu > 0.0f ? nu * vcoef : INFINITY) : n16 * vcoef;
       if (c16 == 0) {
-        bool over = false;
-        const uint32_t nb = f16_bits_f32(nu, &over);
-        const float n16 = f16_val(nb);
-        f32x4 th = {INFINITY, INFINITY, INFINITY, INFINITY}, cs = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int k = 0; k < K; ++k) th[k] = nu > 0.0f ? nu * tpos[k] : INFINITY;
-#pragma unroll
-        for (int k = 0; k <= K; ++k) cs[k] = n16 * cpos[k];
-        *reinterpret_cast<f32x4 *>(&sm.vth[v][0]) = th;
-        *reinterpret_cast<f32x4 *>(&sm.vth[v][4]) = cs;
         sm.nub[v] = nb;
         const int tok = cur.t0 + v;
         if (tok >= 0 && tok < a.n_new) {
