@@ -176,10 +176,8 @@ def quality_report(w, s, rot, proj, K0, V0, Q, st_d, ln_d, max_len, cap, dst, Kn
     return rep
 
 
-def cpu_baseline(w, rot, proj, seconds):
-    """Time the oracle (float64 NumPy) on a bounded sample of the same workload."""
-    import oracle as O
-    import workloads as W
+def oracle_threads():
+    """Threads the oracle's NumPy/BLAS calls use (the BLAS pool, else the CPUs this process may run on)."""
     cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
@@ -187,6 +185,14 @@ def cpu_baseline(w, rot, proj, seconds):
         cores = max([i.get("num_threads", 0) for i in blas] + [1])
     except Exception:
         pass
+    return cores
+
+
+def cpu_baseline(w, rot, proj, seconds):
+    """Time the oracle (float64 NumPy) on a bounded sample of the same workload."""
+    import oracle as O
+    import workloads as W
+    cores = oracle_threads()
     cb = O.build_codebook(w.bits_mse, 1 / math.sqrt(w.d))
     # decode: one kv head over the full context (oracle-packed cache), G query heads
     T = w.seq_len
@@ -230,13 +236,7 @@ def search_cpu_baseline(w, rot, proj, Qn, n_q, seconds):
     bounded sample of keys."""
     import oracle as O
     import workloads as W
-    cores = len(os.sched_getaffinity(0))
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        cores = max([i.get("num_threads", 0) for i in blas] + [1])
-    except Exception:
-        pass
+    cores = oracle_threads()
     cb = O.build_codebook(w.bits_mse, 1 / math.sqrt(w.d))
     n = 65536
     K = W.to_f64(W.kv_chunk(w, 0, 0, 0, n_tokens=n), w.dtype)
