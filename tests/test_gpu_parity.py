@@ -247,7 +247,9 @@ def test_bits_matrix(wid, bits, sketch):
 
 @pytest.mark.parametrize("wid,n_q,off,n", [(2, 8, 37, 1000), (2, 16, 0, 513), (3, 64, 5, 2000), (5, 8, 70, 700),
                                           (5, 24, 0, 64), (1, 8, 1, 1), (1, 16, 3, 900), (2, 48, 11, 3000),
-                                          (2, 512, 9, 300)])
+                                          (2, 512, 9, 300),
+                                          # more than 1024 blocks: the two-slot ring, 16- and 8-query groups
+                                          (2, 512, 0, 40000), (2, 88, 21, 100000)])
 def test_score_keys(wid, n_q, off, n):
     """Search scores of n_q queries against the packed keys of one kv head (slots
     start + off .. + n), compared per entry with the oracle's <q, x_hat> from the
