@@ -1,0 +1,67 @@
+"""CPU tests of the bench's host-side bookkeeping: record sizes and the HBM traffic
+table built from rocprofv3 counter CSVs (no GPU, no kernel)."""
+import csv
+import json
+import os
+
+import pytest
+
+import bench
+
+
+def test_packed_record_bytes():
+    # b' index planes of d bits + m sign bits + two fp16 scales
+    assert bench.packed_record_bytes(128, 128, 2, 1) == 52
+    assert bench.packed_record_bytes(128, 128, 3, 1) == 68
+    assert bench.packed_record_bytes(256, 256, 1, 1) == 68
+    assert bench.packed_record_bytes(128, 128, 3, 0) == 52
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (name, kib) in enumerate(rows):
+            w.writerow([i, name, counter, kib])
+
+
+@pytest.fixture
+def tmp_root(tmp_path, monkeypatch):
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_hash", lambda: "feedface")
+    return tmp_path
+
+
+def test_traffic_scaling_and_lookup(tmp_root, monkeypatch):
+    """Counters in KiB per dispatch, scaled by what they read for a 1 GiB copy; the median
+    dispatch of each kernel is kept; workloads accumulate in one file."""
+    q = "void tq::(anonymous namespace)::quantize_mfma<3, false>(tq::QuantArgs)"
+    d = "void tq::(anonymous namespace)::decode_partial_fast<128, 1, 3, 3, true, false>(tq::DecodeArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    p = {k: str(tmp_root / f"{k}.csv") for k in ("f", "w", "cf", "cw", "f2", "w2")}
+    gib_kib = (1 << 30) / 1024
+    _counter_csv(p["cf"], "FETCH_SIZE", [(copy, gib_kib / 2)] * 3 + [("small", 1.0)])  # reads counted at half
+    _counter_csv(p["cw"], "WRITE_SIZE", [(copy, gib_kib)] * 3)
+    _counter_csv(p["f"], "FETCH_SIZE", [(q, 100.0), (q, 1000.0), (q, 101.0), (d, 50.0)])
+    _counter_csv(p["w"], "WRITE_SIZE", [(q, 10.0), (q, 10.0), (q, 10.0), (d, 2.0)])
+    bench.write_traffic(p["f"], p["w"], p["cf"], p["cw"], copy_bytes=1 << 30, workload="wl-a")
+    t = json.load(open(tmp_root / "profiles" / "traffic.json"))
+    assert t["fetch_scale"] == pytest.approx(2.0) and t["write_scale"] == pytest.approx(1.0)
+    k = t["workloads"]["wl-a"]["kernels"]["quantize_mfma<3, false>"]
+    assert k["fetch_bytes"] == pytest.approx(101.0 * 1024 * 2)      # median of 100, 101, 1000
+    assert k["write_bytes"] == pytest.approx(10.0 * 1024)
+    assert bench.traffic_for([("quantize", 2)], "wl-a") == pytest.approx(2 * (101.0 * 2048 + 10240))
+    assert bench.traffic_for([("quantize", 1), ("decode_partial", 1)], "wl-a") == pytest.approx(
+        101.0 * 2048 + 10240 + 50.0 * 2048 + 2048)
+    assert bench.traffic_for([("decode_merge", 1)], "wl-a") is None  # kernel not counted
+    assert bench.traffic_for([("quantize", 1)], "wl-b") is None      # workload not counted
+    # a second workload joins the file; the first stays
+    _counter_csv(p["f2"], "FETCH_SIZE", [(d, 7.0)])
+    _counter_csv(p["w2"], "WRITE_SIZE", [(d, 1.0)])
+    bench.write_traffic(p["f2"], p["w2"], p["cf"], p["cw"], copy_bytes=1 << 30, workload="wl-b")
+    assert bench.traffic_for([("decode_partial", 1)], "wl-b") == pytest.approx(7.0 * 2048 + 1024)
+    assert bench.traffic_for([("quantize", 1)], "wl-a") is not None
+    # entries taken on other kernel sources are not used
+    monkeypatch.setattr(bench, "source_hash", lambda: "0ther")
+    assert bench.traffic_for([("quantize", 1)], "wl-a") is None
