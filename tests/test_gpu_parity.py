@@ -360,6 +360,45 @@ def test_determinism(wid):
     np.testing.assert_array_equal(o1, o2)
 
 
+def _all_codes(run, starts, n):
+    """Per (tensor, head): codes, signs and fp16 scale values of slots start .. start + n."""
+    out = []
+    for t, (cache, layout, bits) in enumerate(zip(run.host_caches(), (0, 1), (run.k_bits, run.v_bits))):
+        for h in range(run.w.n_kv_heads):
+            i, sg, nb, rb = PR.unpack_tokens(*cache, layout, h, np.arange(starts[0], starts[0] + n), bits)
+            out.append((np.asarray(i), None if sg is None else np.asarray(sg, bool), PR.f16(nb), PR.f16(rb)))
+    return out
+
+
+@pytest.mark.parametrize("wid", [2, 5])
+def test_quantize_symmetries(wid):
+    """Exact symmetries of the device quantize, checked without the oracle: every
+    step is exact or sign-symmetric rounding, so 2x keeps every cell and sign and
+    doubles both fp16 scales, and -x takes the mirrored cells L-1-idx, the flipped
+    signs (a projection exactly 0 keeps its bit) and the same scales."""
+    w = W.WORKLOADS[wid]
+    run = Run(w, batch=1, n_tokens=300)
+    K, V = run.K, run.V
+    dbl = lambda a: W.f32_to_bf16_bits((W.to_f64(a, w.dtype) * 2.0).astype(np.float32))
+    run.quantize(K=K, V=V)
+    base = _all_codes(run, run.starts, 300)
+    run.quantize(K=dbl(K), V=dbl(V))
+    twice = _all_codes(run, run.starts, 300)
+    run.quantize(K=K ^ np.uint16(0x8000), V=V ^ np.uint16(0x8000))
+    neg = _all_codes(run, run.starts, 300)
+    L = 1 << w.bits_mse
+    for (i0, s0, n0, r0), (i1, s1, n1, r1), (i2, s2, n2, r2) in zip(base, twice, neg):
+        np.testing.assert_array_equal(i1, i0)
+        np.testing.assert_array_equal(s1, s0)
+        np.testing.assert_array_equal(n1, 2 * n0)
+        np.testing.assert_array_equal(r1, 2 * r0)
+        np.testing.assert_array_equal(i2, L - 1 - i0)
+        assert np.mean(s2 == s0) < 1e-4          # every sign flips, but for projections exactly 0
+        np.testing.assert_array_equal(n2, n0)
+        np.testing.assert_array_equal(r2, r0)
+    assert run.status() == 0
+
+
 # ------------------------------------------------- full-size, sampled checks ---
 @pytest.mark.parametrize("wid", [2, 3, 5])
 def test_full_workload_sampled(wid):
