@@ -399,6 +399,32 @@ def test_quantize_symmetries(wid):
     assert run.status() == 0
 
 
+@pytest.mark.parametrize("wid", [2, 5])
+def test_decode_symmetries(wid):
+    """Exact symmetries of the device decode, checked without the oracle: the
+    fixed-point exponents are powers of two taken from norms and maxima, so (a) 2q
+    with half the softmax scale gives the same digits and constants, hence the same
+    output bit for bit, and (b) values quantized from 2V give exactly twice the output."""
+    w = W.WORKLOADS[wid]
+    run = Run(w, batch=1, n_tokens=700)
+    run.quantize()
+    starts = torch.from_numpy(np.asarray(run.starts, np.int64)).cuda()
+    lens = torch.from_numpy(run.lens.astype(np.int32)).cuda()
+    dbl = lambda a: W.f32_to_bf16_bits((W.to_f64(a, w.dtype) * 2.0).astype(np.float32))
+    scale = 1.0 / math.sqrt(w.d)
+
+    def dec(q, sm):
+        out = run.s.decode(run.dev(q), starts, lens, run.T, run.kc, run.vc, sm_scale=sm)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    o1 = dec(run.Q, scale)
+    np.testing.assert_array_equal(dec(dbl(run.Q), scale / 2), o1)
+    run.quantize(V=dbl(run.V))
+    np.testing.assert_array_equal(dec(run.Q, scale), 2 * o1)
+    assert run.status() == 0
+
+
 # ------------------------------------------------- full-size, sampled checks ---
 @pytest.mark.parametrize("wid", [2, 3, 5])
 def test_full_workload_sampled(wid):
