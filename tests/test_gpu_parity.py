@@ -404,7 +404,8 @@ def test_decode_symmetries(wid):
     """Exact symmetries of the device decode, checked without the oracle: the
     fixed-point exponents are powers of two taken from norms and maxima, so (a) 2q
     with half the softmax scale gives the same digits and constants, hence the same
-    output bit for bit, and (b) values quantized from 2V give exactly twice the output."""
+    output bit for bit, (b) values quantized from 2V give exactly twice the output, and
+    (c) keys quantized from 2K with half the scale give the same output."""
     w = W.WORKLOADS[wid]
     run = Run(w, batch=1, n_tokens=700)
     run.quantize()
@@ -422,6 +423,29 @@ def test_decode_symmetries(wid):
     np.testing.assert_array_equal(dec(dbl(run.Q), scale / 2), o1)
     run.quantize(V=dbl(run.V))
     np.testing.assert_array_equal(dec(run.Q, scale), 2 * o1)
+    run.quantize(K=dbl(run.K), V=run.V)             # (c) keys from 2K, half the scale: the same scores
+    np.testing.assert_array_equal(dec(run.Q, scale / 2), o1)
+    assert run.status() == 0
+
+
+def test_score_symmetries():
+    """Search scores are exact linear functions of the query digits: 2q gives exactly
+    twice the scores and -q exactly their negation (checked without the oracle)."""
+    w = W.WORKLOADS[2]
+    run = Run(w, batch=1, n_tokens=1500)
+    run.quantize()
+    q = W.f32_to_bf16_bits(np.random.default_rng(5).standard_normal((16, w.d)).astype(np.float32))
+    dbl = W.f32_to_bf16_bits((W.to_f64(q, w.dtype) * 2.0).astype(np.float32))
+    start = int(run.starts[0]) + 3
+
+    def sc(qq):
+        out = run.s.score_keys(run.dev(qq), run.kc, 1, start, 1400)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    s1 = sc(q)
+    np.testing.assert_array_equal(sc(dbl), 2 * s1)
+    np.testing.assert_array_equal(sc(q ^ np.uint16(0x8000)), -s1)
     assert run.status() == 0
 
 
