@@ -428,6 +428,29 @@ def test_decode_symmetries(wid):
     assert run.status() == 0
 
 
+@pytest.mark.parametrize("wid", [2, 5])
+def test_appends_equal_bulk(wid):
+    """A context quantized in appends of assorted sizes (partial 32-slot blocks, written
+    with per-bit atomics in the value layout) leaves the same cache bytes as one bulk
+    call: a vector's codes do not depend on the tile it lands in (checked without the oracle)."""
+    w = W.WORKLOADS[wid]
+    T = 200
+    run = Run(w, batch=1, n_tokens=T)
+    run.quantize()
+    bulk = [x.copy() for c in run.host_caches() for x in c if x is not None]
+    for c in (run.kc, run.vc):
+        c.idx.zero_(); c.sgn.zero_(); c.scl.zero_()
+    off = 0
+    for n in (1, 7, 32, 3, 64, 45, 48):
+        run.quantize(K=run.K[:, :, off:off + n], V=run.V[:, :, off:off + n], dst=run.starts + off)
+        off += n
+    assert off == T
+    appended = [x for c in run.host_caches() for x in c if x is not None]
+    for a, b in zip(bulk, appended):
+        np.testing.assert_array_equal(a, b)
+    assert run.status() == 0
+
+
 def test_score_symmetries():
     """Search scores are exact linear functions of the query digits: 2q gives exactly
     twice the scores and -q exactly their negation (checked without the oracle)."""
