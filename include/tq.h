@@ -174,6 +174,9 @@ int tq_prepare(const float *rot_host, const float *proj_host, int32_t d, int32_t
  * k, v: device [batch][n_kv_heads][n_new][d] in dtype dt (either may be NULL
  * to skip that tensor).  Vector (b, h, t) is written to slot dst_token[b] + t
  * of head h of kc (keys) / vc (values).  dst_token: device int64 [batch].
+ * The ranges [dst_token[b], dst_token[b] + n_new) of different b must not
+ * overlap: overlapping writes race and leave either vector's record.  (A
+ * ragged prefill is one call per sequence, or n_new padded into reserved slots.)
  * status: device uint32 (may be NULL) receiving TQ_FLAG_* bits.
  * dbg_scales: device fp32 [2][batch][n_kv_heads][n_new][2] or NULL; receives
  * the unrounded (||x||, ||r||) of each vector (tensor 0 = keys, 1 = values).
