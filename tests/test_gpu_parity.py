@@ -451,6 +451,34 @@ def test_appends_equal_bulk(wid):
     assert run.status() == 0
 
 
+@pytest.mark.parametrize("wid,batch,T", [(2, 1, 3000), (5, 2, 1500), (4, 64, 2000)])
+def test_workspace_contents_do_not_matter(wid, batch, T):
+    """Decode reads only what it wrote into the workspace: pre-filled with zeros, NaN
+    bit patterns or random bytes, it gives the same output bit for bit (deep and
+    two-slot rings; per-head and grouped query prep and merge at workload 4's shape)."""
+    w0 = W.WORKLOADS[wid]
+    w = W.small(w0, batch=batch, seq_len=T, **({"min_len": T // 3} if w0.ragged else {}))
+    lens = W.seq_lengths(w) if w.ragged else None
+    run = Run(w, batch=batch, n_tokens=None if lens is not None else T, lens=lens)
+    for b in range(batch):               # one call per sequence (ragged lengths)
+        n = int(run.lens[b])
+        run.quantize(K=run.K[b:b + 1, :, :n], V=run.V[b:b + 1, :, :n], dst=run.starts[b:b + 1])
+    ws = run.s.workspace(batch, run.T)
+    starts = torch.from_numpy(np.asarray(run.starts, np.int64)).cuda()
+    lens_d = torch.from_numpy(run.lens.astype(np.int32)).cuda()
+    outs = []
+    for fill in (lambda: ws.zero_(), lambda: ws.fill_(0xFF),
+                 lambda: ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda"))):
+        fill()
+        out = run.s.decode(run.dev(run.Q), starts, lens_d, run.T, run.kc, run.vc, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.isfinite(outs[0]).all()
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+    assert run.status() == 0
+
+
 def test_score_symmetries():
     """Search scores are exact linear functions of the query digits: 2q gives exactly
     twice the scores and -q exactly their negation (checked without the oracle)."""
