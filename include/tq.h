@@ -36,15 +36,19 @@
  *     tokens of the sequence, query head h reading kv head h / G.
  *
  * Conventions for every call:
- *   - Ownership: the caller allocates and frees every buffer.  libtq keeps no
- *     global state, allocates nothing and never synchronizes.  Host structs
- *     are only read during the call.
+ *   - Ownership: the caller allocates and frees every buffer.  libtq
+ *     allocates nothing and never synchronizes; the only state it keeps
+ *     between calls is a per-process cache of each quantize kernel's
+ *     occupancy (a property of the device).  Host structs are only read
+ *     during the call.
  *   - Device calls enqueue work on `stream` and return at once.  Argument
  *     errors are returned synchronously as negative tq_status values and
  *     nothing is enqueued.  A launch failure returns TQ_ERR_LAUNCH.
  *     Data-dependent conditions never fail a call: they set bits in the
  *     caller's device status word (OR-ed, never cleared by libtq).
- *   - Device pointers must be 16-byte aligned.
+ *   - Device pointers must be 16-byte aligned unless the call says otherwise
+ *     (status words, sequence lengths and search scores: 4 bytes; sequence
+ *     starts and destination slots: 8 bytes).
  *   - Reentrant: concurrent calls on different streams with disjoint outputs
  *     are safe.
  */
