@@ -34,6 +34,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "tq_common.h"
@@ -562,12 +563,16 @@ int launch_q(const QuantArgs &a, hipStream_t s) {
   const int64_t tpb = (int64_t(a.n_new) + QT - 1) / QT + 1;
   const int64_t n_tiles = int64_t(a.batch) * a.H * tpb;
   if (n_tiles >= (int64_t(1) << 31)) return 1;
-  static int per_cu = 0;
+  // work-groups per CU: a property of the kernel and device, queried once per
+  // process (an atomic, so that concurrent first calls do not race)
+  static std::atomic<int> per_cu_cache{0};
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, quantize_mfma<BQ, F32>, QN, 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
+    per_cu_cache.store(nb, std::memory_order_relaxed);
   }
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
