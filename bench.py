@@ -16,6 +16,10 @@ Prints one JSON line.  value = packed-KV decode-attention GB/s (algorithmic
 packed bytes read per decode / decode time); the quantize rate (token
 positions per second, each position = K and V of every kv head) is reported
 beside it.  Kernel durations come from HIP events on the launch stream.
+
+Other modes: --workload 5 (d = 256, 64K tokens x 2); --search (inner-product
+search over a 2^23-key packed index, tq_score_keys); --calibrate-copy and
+--traffic (HBM counter calibration and the traffic table, for the profiles).
 """
 from __future__ import annotations
 
