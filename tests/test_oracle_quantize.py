@@ -48,18 +48,53 @@ def test_nearest_centroid_brute_force_d4():
 
 
 def test_cell_rule_on_and_around_midpoints():
-    """u exactly on a threshold goes to the upper cell; one ulp below stays in the lower one."""
+    """The oracle's own cell rule at exact ties: u exactly on a threshold t_k goes to the
+    upper cell k + 1 (idx = #{k : u >= t_k}); one ulp below stays in cell k, one ulp
+    above goes to k + 1.  Checked on the oracle's cell function itself, for every
+    threshold of every width, not on a library search."""
+    from oracle.quantize import _cells
+    for d in (4, 128, 256):
+        for bits in (1, 2, 3):
+            cb = _cb(bits, d)
+            t = np.asarray(cb["boundaries"], np.float64)
+            for k, tk in enumerate(t):
+                u = np.array([tk, np.nextafter(tk, -np.inf), np.nextafter(tk, np.inf)])
+                np.testing.assert_array_equal(_cells(u, t), [k + 1, k, k + 1])
+            # 0 is the middle threshold of every symmetric codebook: a tie there takes L/2
+            L = cb["levels"]
+            assert t[L // 2 - 1] == 0.0
+            np.testing.assert_array_equal(_cells(np.array([0.0, -0.0]), t), [L // 2, L // 2])
+
+
+def test_cell_rule_ties_through_quantize():
+    """Ties reached through the whole quantizer.  With the identity rotation, x = e_0
+    has u = (1, 0, 0, 0): three coordinates sit exactly on the middle threshold 0 and
+    must take the upper cell L/2.  The smallest subnormal +-s put u = +-s, one ulp on
+    either side of that threshold: cells L/2 and L/2 - 1.  A scale of x by a power of
+    two leaves u exactly unchanged, so 4 e_0 gives the same cells."""
+    d = 4
+    tiny = np.nextafter(0.0, 1.0)
+    for bits in (1, 2, 3):
+        cb = _cb(bits, d)
+        L = cb["levels"]
+        x = np.array([[1.0, 0.0, 0.0, 0.0],
+                      [4.0, 0.0, -0.0, 0.0],
+                      [1.0, tiny, -tiny, 0.0]])
+        q = quantize(x, np.eye(d), np.eye(d), cb)
+        top = int(np.sum(1.0 >= np.asarray(cb["boundaries"])))      # u = 1 is above every threshold
+        assert top == L - 1
+        np.testing.assert_array_equal(q["idx"][0], [L - 1, L // 2, L // 2, L // 2])
+        np.testing.assert_array_equal(q["idx"][1], [L - 1, L // 2, L // 2, L // 2])
+        np.testing.assert_array_equal(q["idx"][2], [L - 1, L // 2, L // 2 - 1, L // 2])
+
+
+def test_cell_rule_identity_rotation_is_sorted_search():
+    """Identity rotation: cells reduce to the scalar quantizer on x / ||x||, i.e. a
+    right-sided sorted search of the thresholds (random data, no ties)."""
     d = 4
     for bits in (1, 2, 3):
         cb = _cb(bits, d)
         t = cb["boundaries"]
-        for k, tk in enumerate(t):
-            for u, want in ((tk, k + 1), (np.nextafter(tk, -np.inf), k), (np.nextafter(tk, np.inf), k + 1)):
-                # identity rotation, x = (u, pad) scaled so that x / ||x|| has u in coordinate 0
-                # is not exact in floating point; test the rule through the identity-rotation
-                # special case instead, where cells reduce to a sorted search
-                assert np.searchsorted(t, u, side="right") == want
-        # identity rotation: quantize reduces to the scalar quantizer on x / ||x||
         rng = np.random.default_rng(5)
         x = rng.standard_normal((5000, d))
         q = quantize(x, np.eye(d), np.eye(d), cb)
