@@ -37,10 +37,8 @@
  *
  * Conventions for every call:
  *   - Ownership: the caller allocates and frees every buffer.  libtq
- *     allocates nothing and never synchronizes; the only state it keeps
- *     between calls is a per-process cache of each quantize kernel's
- *     occupancy (a property of the device).  Host structs are only read
- *     during the call.
+ *     allocates nothing, never synchronizes and keeps no state between calls.
+ *     Host structs are only read during the call.
  *   - Device calls enqueue work on `stream` and return at once.  Argument
  *     errors are returned synchronously as negative tq_status values and
  *     nothing is enqueued.  A launch failure returns TQ_ERR_LAUNCH.
@@ -197,16 +195,28 @@ int tq_quantize_kv(const tq_config *cfg, const void *k, const void *v, tq_dtype 
 size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t max_len);
 
 /* Decode attention over the packed caches (one new query per sequence and
- * query head).  q: device [batch][n_q_heads][d] in dtype dt.  Sequence s
- * occupies slots [seq_start[s], seq_start[s] + seq_len[s]) of both caches
- * (device int64 [batch] and int32 [batch]); max_len >= every seq_len is the
- * host-side bound that sizes the launch.  kc must be TOKEN_MAJOR and vc
- * BLOCK32 (TQ_ERR_UNSUPPORTED otherwise).  sm_scale 0 means 1/sqrt(d).
- * out: device fp32 [batch][n_q_heads][d].  A sequence of length 0 yields
- * zeros; a range outside the capacity is clipped and flagged in *status (may
- * be NULL).  workspace: device, >= tq_decode_workspace_bytes bytes.
- * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED,
- * TQ_ERR_LAUNCH. */
+ * query head).  The pages place the method's speed-up in decode, which reads
+ * the compressed cache and so moves less data between memory and the GPU
+ * (ast-softpro.ru, "Технология TurboQuant и её применение с локальными LLM",
+ * section 1.3); the attention itself is not defined there, so the standard
+ * scaled dot-product form is taken: out = softmax(q . k~ * sm_scale) . v~ over
+ * every cached token of the sequence, with k~, v~ the vectors the records
+ * encode (section 1.2: nu~ Pi^T c[idx] + sqrt(pi/2)/m rho~ S^T sgn) and query
+ * head h reading kv head h / G, G = n_q_heads / n_kv_heads (any G <= 16; the
+ * matrix-core kernels take G = 4 and 8 at d = 128 and 256, every other shape
+ * runs the reference-grade kernels).
+ * q: device [batch][n_q_heads][d] in dtype dt.  Sequence s occupies slots
+ * [seq_start[s], seq_start[s] + seq_len[s]) of both caches (device int64
+ * [batch] and int32 [batch]); max_len is the host-side bound on every seq_len
+ * that sizes the launch and the workspace (a longer sequence is cut to its
+ * first max_len tokens and flagged TQ_FLAG_OUT_OF_RANGE).  kc must be
+ * TOKEN_MAJOR and vc BLOCK32 (TQ_ERR_UNSUPPORTED otherwise).  sm_scale 0
+ * means 1/sqrt(d).  out: device fp32 [batch][n_q_heads][d].  A sequence of
+ * length 0 yields zeros; a range outside the capacity is clipped and flagged
+ * in *status (may be NULL).  workspace: device, >= tq_decode_workspace_bytes
+ * bytes, caller-owned; its contents on entry do not matter.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (G > 16,
+ * wrong layouts), TQ_ERR_LAUNCH. */
 int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_t batch,
                         const int64_t *seq_start, const int32_t *seq_len, int32_t max_len,
                         const tq_cache *kc, const tq_cache *vc, float sm_scale, float *out,

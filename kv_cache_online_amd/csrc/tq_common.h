@@ -105,6 +105,7 @@ struct DecodeArgs {
   int32_t batch, Hkv, Hq, G;
   const int64_t *seq_start;
   const int32_t *seq_len;
+  int32_t max_len;       // host bound on seq_len: longer sequences are clipped and flagged
   float sm_scale;
   float kappa;           // sqrt(pi/2) / m
   const float *rot;      // Pi [d][d]

@@ -18,11 +18,13 @@
 //    sketched query, softmax weight times scale) becomes F = rint(v 2^E) with
 //    |F| < 2^30, written as four signed base-256 digits (bytes of
 //    (F + 0x808080) ^ 0x808080).  Rows of the MFMA are (query head, digit), so
-//    16 rows hold 4 heads; G = 8 uses two row blocks.  Digit sums are recombined
-//    exactly in float64.
-//  * Exact split maximum.  Scores of a split (at most 8192 / G slots) are kept in
-//    LDS; the value pass runs after the split's maximum is known, so the integer
-//    accumulators never need rescaling.
+//    16 rows hold 4 heads; G = 8 uses two row blocks.  A score's digit sums and
+//    its +-1 correction are recombined exactly in int32 and rounded once to
+//    fp32; a value accumulator's in float64 at the end of the split.
+//  * Exact split maximum.  A split is at most 1024 slots; its scores stay in
+//    the registers of the lanes that computed them, and the value pass runs
+//    after the split's maximum is known, so the integer accumulators never need
+//    rescaling.
 //
 // Keys are read token-major (a token's planes contiguous: the score contraction
 // runs over coordinates); values in the 32-slot transposed layout (a word holds
@@ -102,6 +104,7 @@ __device__ inline void clip_seq(const DecodeArgs &a, int b, int64_t *start, int6
   if (n < 0) { n = 0; bad = true; }
   if (s < 0 || s > cap) { s = 0; n = 0; bad = true; }
   if (s + n > cap) { n = cap - s; bad = true; }
+  if (!fixed && n > a.max_len) { n = a.max_len; bad = true; }  // the launch covers max_len slots
   if (bad && a.status && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicOr(a.status, TQ_FLAG_OUT_OF_RANGE);
   *start = s;
   *len = n;

@@ -449,7 +449,7 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
   if (kc->layout != TQ_LAYOUT_TOKEN_MAJOR || vc->layout != TQ_LAYOUT_BLOCK32) return TQ_ERR_UNSUPPORTED;
   if (!(sm_scale >= 0) || !std::isfinite(sm_scale)) return TQ_ERR_INVALID_ARG;
   const int G = cfg->n_q_heads / cfg->n_kv_heads;
-  if (G > 16 || (G & (G - 1))) return TQ_ERR_UNSUPPORTED;
+  if (G > 16) return TQ_ERR_UNSUPPORTED;
   const tq::DecodePlan p = tq::decode_plan(*cfg, batch, max_len);
   if (ws_bytes < p.total) return TQ_ERR_WORKSPACE;
   const tq::PrepLayout L = tq::prep_layout(cfg->d, cfg->m);
@@ -476,6 +476,7 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
   a.G = G;
   a.seq_start = seq_start;
   a.seq_len = seq_len;
+  a.max_len = max_len;
   a.sm_scale = sm_scale > 0 ? sm_scale : static_cast<float>(1.0 / std::sqrt(double(cfg->d)));
   a.qbase = double(a.sm_scale) * 1.4426950408889634;  // log2(e): scores in base 2
   a.kv_fixed = -1;
@@ -597,6 +598,7 @@ int tq_score_keys(const tq_config *cfg, const void *q, tq_dtype dt, int32_t n_q,
   a.seq_len = nullptr;
   a.fix_start = start;
   a.fix_len = n;
+  a.max_len = n;
   a.sm_scale = 1.0f;
   a.qbase = 1.0;  // raw inner products
   a.kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / cfg->m);

@@ -166,6 +166,7 @@ __device__ inline void clip_range(const DecodeArgs &a, int b, int64_t *start, in
   if (n < 0) { n = 0; bad = true; }
   if (s < 0 || s > cap) { s = 0; n = 0; bad = true; }
   if (s + n > cap) { n = cap - s; bad = true; }
+  if (n > a.max_len) { n = a.max_len; bad = true; }  // the launch covers max_len slots
   if (bad && a.status && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicOr(a.status, TQ_FLAG_OUT_OF_RANGE);
   *start = s;
   *len = n;
@@ -175,12 +176,14 @@ __device__ inline void clip_range(const DecodeArgs &a, int b, int64_t *start, in
 // one lane per token, online softmax per query head, then value accumulation
 // with one lane per coordinate.  Output per query head: running max m, sum l,
 // A = sum_t p_t nu16_t c[idx_t] (rotated frame), B = sum_t p_t rho16_t (2 sgn_t - 1).
-template <int D, int G>
+// GM is a power of two >= G = a.G (the group size need not be one).
+template <int D, int GM>
 __global__ __launch_bounds__(64) void decode_partial_plain(DecodeArgs a) {
   constexpr int R = D / kWave, W = D / 32;
-  __shared__ float qr[G][D], qs[G][D];
+  const int G = a.G;
+  __shared__ float qr[GM][D], qs[GM][D];
   __shared__ float ck[TQ_MAX_LEVELS], cv[TQ_MAX_LEVELS];
-  __shared__ float P[G][kWave];
+  __shared__ float P[GM][kWave];
   __shared__ float vnu[kWave], vrho[kWave];
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   int64_t start, len;
@@ -189,15 +192,15 @@ __global__ __launch_bounds__(64) void decode_partial_plain(DecodeArgs a) {
     ck[lane] = a.k.cb.cen[lane];
     cv[lane] = a.v.cb.cen[lane];
   }
-  for (int g = 0; g < G; ++g)
+  for (int g = 0; g < GM; ++g)
     for (int r = 0; r < R; ++r) {
       const size_t o = (size_t(b) * a.Hq + size_t(h) * G + g) * D + lane + kWave * r;
-      qr[g][lane + kWave * r] = a.qr[o];
-      qs[g][lane + kWave * r] = a.qs[o];
+      qr[g][lane + kWave * r] = g < G ? a.qr[o] : 0.0f;
+      qs[g][lane + kWave * r] = g < G ? a.qs[o] : 0.0f;
     }
   __syncthreads();
-  float m[G], l[G], A[G][R], B[G][R];
-  for (int g = 0; g < G; ++g) {
+  float m[GM], l[GM], A[GM][R], B[GM][R];
+  for (int g = 0; g < GM; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.0f;
     for (int r = 0; r < R; ++r) A[g][r] = B[g][r] = 0.0f;
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(64) void decode_partial_plain(DecodeArgs a) {
     const int64_t t = tb + lane;
     const bool valid = t < t1;
     const int64_t slot = start + (valid ? t : tb);
-    float s[G];
+    float s[GM];
     {
       uint32_t kw[3][W], sw[W];
       const int64_t hs = int64_t(h) * kcap + slot;
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(64) void decode_partial_plain(DecodeArgs a) {
         for (int w = 0; w < W; ++w) kw[q][w] = q < a.k.bq ? a.k.idx[(hs * a.k.bq + q) * W + w] : 0u;
       for (int w = 0; w < W; ++w) sw[w] = a.k.sketch ? a.k.sgn[hs * W + w] : 0u;
       const float knu = f16_val(a.k.scl[hs * 2]), krho = f16_val(a.k.scl[hs * 2 + 1]);
-      for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < GM; ++g) {
         float sd = 0.0f, sg = 0.0f;
         for (int j = 0; j < D; ++j) {
           const int w = j >> 5, bt = j & 31;
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(64) void decode_partial_plain(DecodeArgs a) {
       vnu[lane] = valid ? f16_val(a.v.scl[hv * 2]) : 0.0f;
       vrho[lane] = valid ? f16_val(a.v.scl[hv * 2 + 1]) : 0.0f;
     }
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < GM; ++g) {
       const float tmax = wave_max_f(s[g]);
       const float mn = fmaxf(m[g], tmax);
       const float alpha = m[g] == -INFINITY ? 0.0f : expf(m[g] - mn);
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(64) void decode_partial_plain(DecodeArgs a) {
           const int c = ((vw[0][r] >> bt) & 1) | (((vw[1][r] >> bt) & 1) << 1) | (((vw[2][r] >> bt) & 1) << 2);
           const float cvv = cv[c] * vnu[tt];
           const float sgv = ((vs[r] >> bt) & 1) ? vrho[tt] : -vrho[tt];
-          for (int g = 0; g < G; ++g) {
+          for (int g = 0; g < GM; ++g) {
             A[g][r] = fmaf(P[g][tt], cvv, A[g][r]);
             B[g][r] = fmaf(P[g][tt], sgv, B[g][r]);
           }
@@ -335,9 +338,9 @@ int launch_quantize_d(const QuantArgs &a, hipStream_t s) {
   return hipGetLastError() != hipSuccess;
 }
 
-template <int D, int G>
+template <int D, int GM>
 int launch_partial(const DecodeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_partial_plain<D, G>), dim3(a.n_split, a.Hkv, a.batch), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((decode_partial_plain<D, GM>), dim3(a.n_split, a.Hkv, a.batch), dim3(64), 0, s, a);
   return 0;
 }
 
@@ -345,14 +348,13 @@ template <int D>
 int launch_decode_d(const DecodeArgs &a, hipStream_t s) {
   const unsigned nq = static_cast<unsigned>(a.batch * a.Hq);
   hipLaunchKernelGGL(decode_qprep_plain<D>, dim3(nq), dim3(256), 0, s, a);
-  switch (a.G) {
-    case 1: launch_partial<D, 1>(a, s); break;
-    case 2: launch_partial<D, 2>(a, s); break;
-    case 4: launch_partial<D, 4>(a, s); break;
-    case 8: launch_partial<D, 8>(a, s); break;
-    case 16: launch_partial<D, 16>(a, s); break;
-    default: return 1;
-  }
+  // the kernel's head loops run to the next power of two; heads past G are idle
+  if (a.G < 1 || a.G > 16) return 1;
+  if (a.G == 1) launch_partial<D, 1>(a, s);
+  else if (a.G == 2) launch_partial<D, 2>(a, s);
+  else if (a.G <= 4) launch_partial<D, 4>(a, s);
+  else if (a.G <= 8) launch_partial<D, 8>(a, s);
+  else launch_partial<D, 16>(a, s);
   hipLaunchKernelGGL(decode_merge_plain<D>, dim3(nq), dim3(256), 0, s, a);
   return hipGetLastError() != hipSuccess;
 }

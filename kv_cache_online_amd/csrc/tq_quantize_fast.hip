@@ -34,7 +34,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 
 #include "tq_common.h"
@@ -563,17 +562,11 @@ int launch_q(const QuantArgs &a, hipStream_t s) {
   const int64_t tpb = (int64_t(a.n_new) + QT - 1) / QT + 1;
   const int64_t n_tiles = int64_t(a.batch) * a.H * tpb;
   if (n_tiles >= (int64_t(1) << 31)) return 1;
-  // work-groups per CU: a property of the kernel and device, queried once per
-  // process (an atomic, so that concurrent first calls do not race)
-  static std::atomic<int> per_cu_cache{0};
-  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
-  if (per_cu == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, quantize_mfma<BQ, F32>, QN, 0) != hipSuccess || nb < 1)
-      nb = 1;
-    per_cu = nb;
-    per_cu_cache.store(nb, std::memory_order_relaxed);
-  }
+  // Persistent grid of two work-groups per CU, the occupancy the kernel's
+  // registers and LDS are sized for; a grid larger than what fits only queues
+  // (work-groups never wait on each other), so no per-process occupancy query or
+  // cache is needed.
+  constexpr int per_cu = 2;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)

@@ -41,6 +41,12 @@ def quantize_parity(x64, rot, proj, cb, g_idx, g_sgn, g_nu_bits, g_rho_bits, g_d
     rep = {"label": label, "n_vectors": n, "errors": [], "index_mismatch": [], "sign_mismatch": [],
            "scale_near_ties": []}
     t = np.asarray(cb["boundaries"])
+    # entries inside the near-tie band (for the record; only mismatches are listed)
+    rep["index_entries"] = int(o["u"].size)
+    near = np.zeros(o["u"].shape, dtype=bool)
+    for tk in t:
+        near |= np.abs(o["u"] - tk) < BAND * sigma
+    rep["index_near_ties"] = int(near.sum())
     # 1. cell indices
     mm = np.argwhere(g_idx != o["idx"])
     for vi, j in mm:
@@ -82,6 +88,8 @@ def quantize_parity(x64, rot, proj, cb, g_idx, g_sgn, g_nu_bits, g_rho_bits, g_d
         p[cond], rho[cond], rho_bits[cond], sgn[cond] = c["p"], c["rho"], c["rho_bits"], c["sgn"]
     rep["conditioned_vectors"] = int(len(cond))
     # 4. signs
+    rep["sign_entries"] = int(sgn.size)
+    rep["sign_near_ties"] = int(np.sum(np.abs(p) < BAND * rho[:, None]))
     sm = np.argwhere(g_sgn != sgn)
     for vi, i in sm:
         dist = abs(p[vi, i]) / max(rho[vi], 1e-300)
@@ -107,9 +115,27 @@ def quantize_parity(x64, rot, proj, cb, g_idx, g_sgn, g_nu_bits, g_rho_bits, g_d
     return rep
 
 
+def records(rep, meta, tensor):
+    """Every mismatch of a quantize report as a JSON-ready dict.  meta[vi] =
+    (sequence, kv head, token) of compared vector vi."""
+    out = []
+    for vi, j, want, got, dist in rep["index_mismatch"]:
+        s, h, tok = (int(v) for v in meta[vi])
+        out.append({"kind": "index", "tensor": tensor, "sequence": s, "head": h, "token": tok, "coordinate": j,
+                    "oracle": want, "gpu": got, "distance_sigma": dist})
+    for vi, i, want, dist in rep["sign_mismatch"]:
+        s, h, tok = (int(v) for v in meta[vi])
+        out.append({"kind": "sign", "tensor": tensor, "sequence": s, "head": h, "token": tok, "coordinate": i,
+                    "oracle": int(want), "gpu": int(not want), "distance_rho": dist})
+    for kind, vi in rep["scale_near_ties"]:
+        s, h, tok = (int(v) for v in meta[vi])
+        out.append({"kind": f"fp16 {kind}", "tensor": tensor, "sequence": s, "head": h, "token": tok})
+    return out
+
+
 def summary(rep):
-    keys = ("label", "n_vectors", "index_mismatch_frac", "sign_mismatch_frac", "nu_max_rel",
-            "rho_max_rel", "conditioned_vectors")
+    keys = ("label", "n_vectors", "index_entries", "index_near_ties", "index_mismatch_frac", "sign_entries",
+            "sign_near_ties", "sign_mismatch_frac", "nu_max_rel", "rho_max_rel", "conditioned_vectors")
     s = {k: rep.get(k) for k in keys}
     s["n_index_mismatch"] = len(rep["index_mismatch"])
     s["n_sign_mismatch"] = len(rep["sign_mismatch"])

@@ -5,7 +5,9 @@ entry; the full workload shapes are compared on sampled vectors and on sampled
 (sequence, kv head) decode outputs, which the oracle recomputes from the packed
 bytes the device wrote.
 """
+import json
 import math
+import os
 import sys
 
 import numpy as np
@@ -28,6 +30,25 @@ def _need_gpu():
 def _log(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+# Every quantize mismatch (each must be a near-tie) and every decode comparison is
+# written to parity_<workload>.jsonl under this folder, one JSON object a line.
+PARITY_DIR = os.environ.get("TQ_PARITY_DIR", os.path.join(os.path.dirname(os.path.dirname(
+    os.path.abspath(__file__))), "gpurun_out", "parity"))
+_parity_files = set()
+
+
+def _record(workload, objs):
+    os.makedirs(PARITY_DIR, exist_ok=True)
+    path = os.path.join(PARITY_DIR, f"parity_{workload}.jsonl")
+    with open(path, "a" if path in _parity_files else "w") as fh:
+        if path not in _parity_files:
+            import bench
+            fh.write(json.dumps({"kind": "run", "workload": workload, "source_hash": bench.source_hash()}) + "\n")
+        for o in objs:
+            fh.write(json.dumps(o) + "\n")
+    _parity_files.add(path)
 
 
 class Run:
@@ -95,8 +116,9 @@ class Run:
         return int(self.s.status.cpu().numpy()[0]) & 0xFFFFFFFF
 
 
-def check_quantize(run, dbg, samples=None, T=None, K=None, V=None, starts=None, label=""):
-    """Compare (tensor, seq, head, token) vectors; samples=None means every vector."""
+def check_quantize(run, dbg, samples=None, T=None, K=None, V=None, starts=None, label="", per_head=64):
+    """Compare (tensor, seq, head, token) vectors; samples=None means every vector,
+    else per_head tokens of every (sequence, kv head) drawn with seed `samples`."""
     w = run.w
     K = run.K if K is None else K
     V = run.V if V is None else V
@@ -114,7 +136,7 @@ def check_quantize(run, dbg, samples=None, T=None, K=None, V=None, starts=None, 
             sel = []
             for s in range(b):
                 for hh in range(h):
-                    sel.append((s, hh, np.sort(rng.choice(n, size=min(n, 64), replace=False))))
+                    sel.append((s, hh, np.sort(rng.choice(n, size=min(n, per_head), replace=False))))
         xs, gi, gs, gnb, grb, gdbg = [], [], [], [], [], []
         for s, hh, toks in sel:
             slots = starts[s] + toks
@@ -128,7 +150,12 @@ def check_quantize(run, dbg, samples=None, T=None, K=None, V=None, starts=None, 
         rep = PR.quantize_parity(np.concatenate(xs), run.rot, run.proj, cb, np.concatenate(gi),
                                  np.concatenate(gs), np.concatenate(gnb), np.concatenate(grb),
                                  np.concatenate(gdbg), sketch=bool(sk), label=f"{label} tensor {tensor}")
-        _log(PR.summary(rep))
+        meta = np.concatenate([np.stack([np.full(len(tk), sq), np.full(len(tk), hh), tk], axis=1)
+                               for sq, hh, tk in sel])
+        summ = PR.summary(rep)
+        _record(w.name, [{"kind": "quantize summary", **summ}]
+                + [{"label": summ["label"], **r} for r in PR.records(rep, meta, tensor)])
+        _log(summ)
         assert rep["ok"], PR.summary(rep)
         reps.append(rep)
     return reps
@@ -143,6 +170,7 @@ def check_decode(run, out, pairs=None, lens=None, starts=None, label=""):
     if pairs is None:
         pairs = [(s, h) for s in range(run.batch) for h in range(w.n_kv_heads)]
     worst = 0.0
+    recs = []
     for s, h in pairs:
         q64 = W.to_f64(run.Q[s, h * G:(h + 1) * G], w.dtype)
         n = int(lens[s])
@@ -154,7 +182,10 @@ def check_decode(run, out, pairs=None, lens=None, starts=None, label=""):
         vmax = np.max(np.abs(W.to_f64(run.V[s, h, :min(n, run.V.shape[2])], w.dtype)))
         err = np.max(np.abs(out[s, h * G:(h + 1) * G] - ref))
         worst = max(worst, err / vmax)
+        recs.append({"label": label, "kind": "decode", "sequence": int(s), "kv_head": int(h), "length": n,
+                     "max_abs_err": float(err), "max_abs_V": float(vmax), "err_over_maxV": float(err / vmax)})
         assert err <= 1e-4 * vmax, (label, s, h, err, vmax)
+    _record(w.name, recs)
     _log({"label": label, "decode_pairs": len(pairs), "worst_err_over_maxV": worst})
     return worst
 
@@ -502,22 +533,27 @@ def test_score_symmetries():
 
 # ------------------------------------------------- full-size, sampled checks ---
 @pytest.mark.parametrize("wid", [2, 3, 5])
-def test_full_workload_sampled(wid):
+def test_full_workload(wid):
+    """Full workload shapes.  Workload 2: every one of its 524,288 vectors is compared
+    with the oracle; workloads 3 and 5: 1,024 tokens of every (sequence, kv head).
+    Decode: every kv head of sequence 0, plus every kv head of the last sequence."""
     w = W.WORKLOADS[wid]
     _log(f"workload {wid} full: generating inputs")
     run = Run(w)
     _log(f"workload {wid} full: quantize {run.batch}x{w.n_kv_heads}x{run.T}")
     dbg = run.quantize()
-    check_quantize(run, dbg, samples=wid, label=f"w{wid}-full")
+    check_quantize(run, dbg, samples=None if wid == 2 else wid, per_head=1024, label=f"w{wid}-full")
     _log(f"workload {wid} full: decode")
     out = run.decode()
-    rng = np.random.default_rng(wid)
-    pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, run.batch, 2), rng.integers(0, w.n_kv_heads, 2))]
-    check_decode(run, out, pairs=pairs, label=f"w{wid}-full")
     assert run.status() == 0
+    seqs = sorted({0, run.batch - 1})
+    pairs = [(s, h) for s in seqs for h in range(w.n_kv_heads)]
+    check_decode(run, out, pairs=pairs, label=f"w{wid}-full")
 
 
-def test_full_workload4_ragged_sampled():
+def test_full_workload4_ragged():
+    """64 ragged sequences: the incremental quantize of one token per sequence is
+    compared in full; decode over len + 1 on every kv head of three sequences."""
     w = W.WORKLOADS[4]
     lens = W.seq_lengths(w)
     _log("workload 4 full: generating inputs")
@@ -536,18 +572,63 @@ def test_full_workload4_ragged_sampled():
         run.V[s, :, lens[s]] = newv[s, :, 0]
     lens1 = lens + 1
     out = run.decode(lens=lens1)
-    rng = np.random.default_rng(4)
-    pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, w.batch, 3), rng.integers(0, w.n_kv_heads, 3))]
+    assert run.status() == 0
+    seqs = [0, int(np.argmax(lens)), w.batch - 1]
+    pairs = [(s, h) for s in seqs for h in range(w.n_kv_heads)]
     check_decode(run, out, pairs=pairs, lens=lens1, label="w4-full")
 
 
-@pytest.mark.parametrize("d,hkv,hq", [(128, 2, 4), (64, 1, 16)])
+@pytest.mark.parametrize("d,hkv,hq", [(128, 2, 4), (64, 1, 16), (256, 2, 12), (128, 2, 6), (128, 1, 3),
+                                      (128, 1, 1)])
 def test_reference_decode_path(d, hkv, hq):
-    """Shapes outside the matrix-core decode (G = 2; d = 64 with G = 16) run the reference kernels."""
-    w = W.small(W.WORKLOADS[2], d=d, n_kv_heads=hkv, n_q_heads=hq, batch=2, seq_len=300)
+    """Shapes outside the matrix-core decode run the reference kernels: G = 2; d = 64
+    with G = 16; group sizes that are not powers of two, among them GQA 6:1 at
+    head_dim 256 (the shape of the pages' Qwen 3.5 27B example); G = 1."""
+    w = W.small(W.WORKLOADS[5 if d == 256 else 2], d=d, n_kv_heads=hkv, n_q_heads=hq, batch=2, seq_len=300)
     run = Run(w)
     _log(f"reference decode path d={d} G={hq // hkv}")
     dbg = run.quantize()
     check_quantize(run, dbg, label=f"ref-d{d}")
     check_decode(run, run.decode(), label=f"ref-d{d}-G{hq // hkv}")
+    assert run.status() == 0
+
+
+def test_decode_longer_than_max_len_is_clipped():
+    """A sequence longer than the max_len the call was sized for is cut to its first
+    max_len tokens and raises TQ_FLAG_OUT_OF_RANGE (the matrix-core and the reference
+    kernels)."""
+    for wid, hq in ((2, 32), (2, 16)):
+        w = W.small(W.WORKLOADS[wid], n_q_heads=hq, batch=2, seq_len=700)
+        run = Run(w)
+        run.quantize()
+        lens = np.array([700, 300])
+        run.s.status.zero_()
+        out = run.decode(lens=lens, max_len=500)
+        assert run.status() & 4
+        run.s.status.zero_()
+        want = run.decode(lens=np.array([500, 300]), max_len=500)
+        assert run.status() == 0
+        np.testing.assert_array_equal(out, want)
+
+
+@pytest.mark.parametrize("wid", [2, 5])
+def test_adjacent_sequences_share_blocks(wid):
+    """Several sequences in one quantize call with unpadded, adjacent slot ranges,
+    so that neighbours write disjoint bits of the same value-layout words (32-slot
+    blocks): the bytes equal those of one call per sequence, and the oracle's."""
+    w = W.WORKLOADS[wid]
+    n, B = 45, 4
+    run = Run(w, batch=B, n_tokens=n)
+    dst = np.arange(B, dtype=np.int64) * n + 7          # 7, 52, 97, 142: every block boundary is shared
+    assert int(dst[-1]) + n <= run.cap
+    dbg = run.quantize(dst=dst)
+    check_quantize(run, dbg, starts=dst, label=f"w{wid}-adjacent")
+    together = [x.copy() for c in run.host_caches() for x in c if x is not None]
+    for c in (run.kc, run.vc):
+        c.idx.zero_(); c.sgn.zero_(); c.scl.zero_()
+    for b in range(B):
+        run.quantize(K=run.K[b:b + 1], V=run.V[b:b + 1], dst=dst[b:b + 1])
+    apart = [x for c in run.host_caches() for x in c if x is not None]
+    for a, b in zip(together, apart):
+        np.testing.assert_array_equal(a, b)
     assert run.status() == 0

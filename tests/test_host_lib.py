@@ -218,7 +218,7 @@ def test_decode_validation():
     assert _dec(cfg, out=FAKE + 8, ws_bytes=1 << 30) == B.TQ_ERR_INVALID_ARG
     assert _dec(cfg, scale=float("nan"), ws_bytes=1 << 30) == B.TQ_ERR_INVALID_ARG
     assert _dec(cfg, kc=_cache(B.TQ_LAYOUT_BLOCK32, 8192), ws_bytes=1 << 30) == B.TQ_ERR_UNSUPPORTED
-    bad = _cfg(hq=24)   # G = 3
+    bad = _cfg(hq=136)   # G = 17: more query heads per kv head than the kernels take
     assert _dec(bad, ws_bytes=1 << 30) == B.TQ_ERR_UNSUPPORTED
 
 
