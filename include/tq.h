@@ -222,6 +222,27 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
                         const tq_cache *kc, const tq_cache *vc, float sm_scale, float *out,
                         uint32_t *status, void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the fixed device scratch behind tq_decode_attention_noalloc (per device). */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* tq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and outputs as
+ * tq_decode_attention; the workspace is a fixed TQ_NOALLOC_SCRATCH_BYTES array
+ * inside the library, one per device, held from when the library's code is
+ * loaded on the device until the process ends.  The call allocates nothing.
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (other streams, other threads) race and must be serialized by the
+ * caller.  Returns TQ_ERR_WORKSPACE when tq_decode_workspace_bytes(cfg, batch,
+ * max_len) exceeds the array (for example 256 query heads over 128K tokens need
+ * about 35 MB, 2,048 query heads over 16K tokens about 38 MB), TQ_ERR_LAUNCH if
+ * the array's address cannot be found on the current device, and otherwise
+ * what tq_decode_attention returns. */
+int tq_decode_attention_noalloc(const tq_config *cfg, const void *q, tq_dtype dt, int32_t batch,
+                                const int64_t *seq_start, const int32_t *seq_len, int32_t max_len,
+                                const tq_cache *kc, const tq_cache *vc, float sm_scale, float *out,
+                                uint32_t *status, hipStream_t stream);
+
 /* Workspace bytes tq_score_keys needs for n_q queries over at most max_n keys. */
 size_t tq_score_workspace_bytes(const tq_config *cfg, int32_t n_q, int32_t max_n);
 

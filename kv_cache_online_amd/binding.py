@@ -24,8 +24,9 @@ TQ_FLAG_NONFINITE_INPUT, TQ_FLAG_SCALE_OVERFLOW, TQ_FLAG_OUT_OF_RANGE = 1, 2, 4
 TQ_MAX_LEVELS = 8
 
 EXPORTED = ("tq_build_codebook", "tq_build_codebook_sphere", "tq_prepare_bytes", "tq_prepare", "tq_quantize_kv",
-            "tq_decode_workspace_bytes", "tq_decode_attention", "tq_score_workspace_bytes", "tq_score_keys",
-            "tq_status_string")
+            "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_noalloc",
+            "tq_score_workspace_bytes", "tq_score_keys", "tq_status_string")
+TQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class tq_codebook(Structure):
@@ -80,6 +81,10 @@ def _load():
                                         c_void_p, c_int32, POINTER(tq_cache), POINTER(tq_cache),
                                         c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.tq_decode_attention.restype = c_int
+    lib.tq_decode_attention_noalloc.argtypes = [POINTER(tq_config), c_void_p, c_int, c_int32, c_void_p,
+                                                c_void_p, c_int32, POINTER(tq_cache), POINTER(tq_cache),
+                                                c_float, c_void_p, c_void_p, c_void_p]
+    lib.tq_decode_attention_noalloc.restype = c_int
     lib.tq_score_workspace_bytes.argtypes = [POINTER(tq_config), c_int32, c_int32]
     lib.tq_score_workspace_bytes.restype = c_size_t
     lib.tq_score_keys.argtypes = [POINTER(tq_config), c_void_p, c_int, c_int32, POINTER(tq_cache), c_int32,
@@ -166,6 +171,15 @@ def tq_decode_attention(cfg: tq_config, q, dt: int, batch: int, seq_start, seq_l
                                  _ptr(status), _ptr(workspace), ws_bytes, _stream(stream))
     if st != TQ_OK:
         raise TQError(st, "tq_decode_attention")
+
+
+def tq_decode_attention_noalloc(cfg: tq_config, q, dt: int, batch: int, seq_start, seq_len, max_len: int,
+                                kc: tq_cache, vc: tq_cache, sm_scale: float, out, status, stream=None) -> None:
+    st = LIB.tq_decode_attention_noalloc(ctypes.byref(cfg), _ptr(q), dt, batch, _ptr(seq_start), _ptr(seq_len),
+                                         max_len, ctypes.byref(kc), ctypes.byref(vc), sm_scale, _ptr(out),
+                                         _ptr(status), _stream(stream))
+    if st != TQ_OK:
+        raise TQError(st, "tq_decode_attention_noalloc")
 
 
 def tq_score_workspace_bytes(cfg: tq_config, n_q: int, max_n: int) -> int:
