@@ -42,6 +42,7 @@ namespace tq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kSigPlane = 4;     // operand / accumulator slot of the sign plane
@@ -96,9 +97,18 @@ __device__ inline uint32_t digits(int32_t f) { return static_cast<uint32_t>(f + 
 // Exponent E with vmax * 2^E < 2^30 (0 for vmax == 0).
 __device__ inline int fix_exp(double vmax) { return vmax > 0.0 ? 29 - ilogb(vmax) : 0; }
 
+// A wave-uniform read of memory that no kernel of the launch writes, through the
+// scalar cache (constant address space): the clipping below then runs on the
+// scalar unit instead of the vector ALU.
+template <typename T>
+__device__ inline T load_uniform(const T *p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T *>(reinterpret_cast<uintptr_t>(p));
+}
+
 __device__ inline void clip_seq(const DecodeArgs &a, int b, int64_t *start, int64_t *len) {
   const bool fixed = a.seq_start == nullptr;  // key scoring: one slot range, keys only
-  int64_t s = fixed ? a.fix_start : a.seq_start[b], n = fixed ? a.fix_len : a.seq_len[b];
+  int64_t s = fixed ? a.fix_start : load_uniform(a.seq_start + b);
+  int64_t n = fixed ? a.fix_len : load_uniform(a.seq_len + b);
   const int64_t cap = fixed ? a.k.cap : a.k.cap < a.v.cap ? a.k.cap : a.v.cap;
   bool bad = false;
   if (n < 0) { n = 0; bad = true; }
@@ -190,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 32 * w + 8 * i + sv + 4 * h;
-        const int32_t F = static_cast<int32_t>(rintf(ldexpf(wk * vals[j - c0], E - sv)));
+        const int32_t F = 2 * static_cast<int32_t>(rintf(ldexpf(wk * vals[j - c0], E - 1 - sv)));
         wv[sv] |= ((digits(F) >> (8 * l)) & 0xFFu) << (8 * i);
       }
     const int slot = sgn ? kSigPlane : pidx;
@@ -200,8 +210,8 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
     // alpha (Walsh planes) or beta (sign plane, 0 without one): the scale of the digit sums
     const double base = a.qbase;  // sm_scale log2(e) (scores in base 2), or 1 for raw scores
     int32_t *qc = a.qconst + size_t(bh) * 8;
-    if (sgn) qc[5] = __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), -E)));
-    else qc[4] = __float_as_int(static_cast<float>(ldexp(base, -E)));
+    if (sgn) qc[5] = __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), 1 - E)));
+    else qc[4] = __float_as_int(static_cast<float>(ldexp(base, 1 - E)));
     if (!sgn && !a.k.sketch) qc[5] = 0;
   }
 }
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 32 * w + 8 * i + sv + 4 * hh;
-        const int32_t F = static_cast<int32_t>(rintf(ldexpf(wk * vals[h][j - c0], E - sv)));
+        const int32_t F = 2 * static_cast<int32_t>(rintf(ldexpf(wk * vals[h][j - c0], E - 1 - sv)));
         wv[sv] |= ((digits(F) >> (8 * l)) & 0xFFu) << (8 * i);
       }
     const int slot = sgn ? kSigPlane : pidx;
@@ -294,8 +304,8 @@ __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq
       const int E = fix_exp(scale * double(qn[tid]) * (1.0 + 0x1p-10));
       const double base = a.qbase;  // sm_scale log2(e) (scores in base 2), or 1 for raw scores
       int32_t *qc = a.qconst + size_t(bh) * 8;
-      if (sgn) qc[5] = __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), -E)));
-      else qc[4] = __float_as_int(static_cast<float>(ldexp(base, -E)));
+      if (sgn) qc[5] = __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), 1 - E)));
+      else qc[4] = __float_as_int(static_cast<float>(ldexp(base, 1 - E)));
       if (!sgn && !a.k.sketch) qc[5] = 0;
     }
   }
@@ -378,15 +388,16 @@ __device__ inline void lds_barrier() {
 
 __device__ inline uint32_t lds32(const unsigned char *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
-// Score digit sums to 2 x - k exactly, then fp32: x = lo + 2^16 hi with
-// lo = c0 + 2^8 c1, hi = c2 + 2^8 c3, and k = 2^17 KH + KL (0 <= KL < 2^17), so
-// 2 x - k = 2^17 (hi - KH) + (2 lo - KL), both parts exact in int32.
-__device__ inline float score_sum(v4i c, int32_t KH, int32_t KL) {
+// A score accumulator's four digit slots c_l, each below 2^19 in magnitude, hold
+// the +-1 form sum_l 256^l c_l (see the corrections below): the pairs
+// lo = c0 + 2^8 c1 and hi = c2 + 2^8 c3 are exact in int32, and 2^16 hi + lo is
+// rounded to fp32.
+__device__ inline float score_sum(v4i c) {
   const int32_t lo = c.x + (c.y << 8), hi = c.z + (c.w << 8);
-  return fmaf(static_cast<float>(hi - KH), 131072.0f, static_cast<float>(2 * lo - KL));
+  return fmaf(static_cast<float>(hi), 65536.0f, static_cast<float>(lo));
 }
 
-template <int D, int RB, int BQK, int BQV, bool DEEP>
+template <int D, int RB, int BQK, int BQV, int SLOTS_, int AWP_>
 struct SplitShape {
   static constexpr int C = D / 64, W = D / 32, NB = D / 64, NW = D / 128, G = 4 * RB;
   static constexpr int PK = BQK == 3 ? 4 : BQK, PV = BQV == 3 ? 4 : BQV;
@@ -399,27 +410,24 @@ struct SplitShape {
   static constexpr int SLOT = K_BYTES > V_BYTES ? K_BYTES : V_BYTES;
   static constexpr int NI_K = (BQK + 1) * NW + 2, NI_V = (BQV + 1) * NW;  // loads per chunk
   static constexpr int NI_MIN = NI_K < NI_V ? NI_K : NI_V;
-  // Ring slots per wave and value operand buffers (round parity).  DEEP (one
-  // head block, few work-groups: latency-bound) keeps two chunks in flight per
-  // wave; otherwise the smaller LDS footprint fits more work-groups per CU, which
-  // hides more (three or four per CU).
-  static constexpr int SLOTS = DEEP ? 3 : 2;
-  static constexpr int AWP = DEEP ? 2 : 1;
+  // Ring slots per wave (SLOTS - 1 chunks in flight) and value operand buffers
+  // (AWP = 2: one per round parity, so a round's operands are written while the
+  // previous round's are still read).
+  static constexpr int SLOTS = SLOTS_;
+  static constexpr int AWP = AWP_;
 };
 
 // SCORES: key scoring (tq_score_keys) -- phase 1 only, over key head a.kv_fixed,
 // writing each score instead of the split's attention partial.
-template <int D, int RB, int BQK, int BQV, bool DEEP, bool SCORES = false>
+template <int D, int RB, int BQK, int BQV, int SLOTS, int AWP_, bool SCORES = false>
 __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
-  using P = SplitShape<D, RB, BQK, BQV, DEEP>;
+  using P = SplitShape<D, RB, BQK, BQV, SLOTS, AWP_>;
   constexpr int C = P::C, W = P::W, NB = P::NB, NW = P::NW, G = P::G, PK = P::PK, PV = P::PV;
   constexpr int KREC = P::KREC, KSREC = P::KSREC, VREC = P::VREC, VSREC = P::VSREC, AWP = P::AWP;
   constexpr int kSlots = P::SLOTS;
   __shared__ __attribute__((aligned(16))) unsigned char ring[4][kSlots][P::SLOT];
   // value A operands of a round: [round parity][part][tile][kgroup][rb][row][byte]
   __shared__ __attribute__((aligned(16))) unsigned char aw[AWP][2][4][4][RB][16][16];
-  // per wave: the digit words of its tile (one part at a time) in operand byte order
-  __shared__ __attribute__((aligned(16))) uint32_t fst[4][RB][4][64];
   __shared__ float redf[4][G];
   __shared__ float redv[4][2];
   __shared__ float mh_s[G];
@@ -552,10 +560,19 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   const uint32_t msk[4] = {0x01010101u, 0x02020202u, 0x04040404u, 0x08080808u};
   const v4i ones = {static_cast<int>(msk[0]), static_cast<int>(msk[1]), static_cast<int>(msk[2]),
                     static_cast<int>(msk[3])};
-  // The +-1 corrections k = sum_j F_j 2^shift_j of the index planes (summed) and
-  // of the sign plane: the query operands against all-ones bit planes, exact
-  // digit sums, split as k = 2^17 KH + KL with 0 <= KL < 2^17.
-  int32_t khi[RB], kli[RB], khs[RB], kls[RB];
+  // The query operands are even integers G_j = 2 F_j, so the plane products sum
+  // to x = sum_j G_j b_j 2^shift_j = 2 sum_j F_j b_j 2^shift_j.  The +-1
+  // correction k = sum_j F_j 2^shift_j, exactly half the operands' digit sums
+  // against all-ones planes (index planes summed; sign plane), is loaded into
+  // every score accumulator as -k, spread over the four digit slots (three
+  // bytes and the rest), so each slot ends at a sum below 2^19 whose weighted
+  // total sum_l 256^l c_l is the +-1 form x - k.
+  v4i nki[RB], nks[RB];
+  auto neg_half = [](v4i c) {
+    const int64_t k = (int64_t(c.x) + (int64_t(c.y) << 8) + (int64_t(c.z) << 16) + (int64_t(c.w) << 24)) >> 1;
+    return v4i{-static_cast<int>(k & 0xFF), -static_cast<int>((k >> 8) & 0xFF), -static_cast<int>((k >> 16) & 0xFF),
+               -static_cast<int>(k >> 24)};
+  };
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     v4i ci = {0, 0, 0, 0}, cs = {0, 0, 0, 0};
@@ -565,21 +582,20 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
       for (int p = 0; p < PK; ++p) ci = mfma(qa[rb][p][c], ones, ci);
       cs = mfma(qa[rb][PK][c], ones, cs);
     }
-    const int64_t ki = int64_t(ci.x) + (int64_t(ci.y) << 8) + (int64_t(ci.z) << 16) + (int64_t(ci.w) << 24);
-    const int64_t ks = int64_t(cs.x) + (int64_t(cs.y) << 8) + (int64_t(cs.z) << 16) + (int64_t(cs.w) << 24);
-    khi[rb] = static_cast<int32_t>(ki >> 17);
-    kli[rb] = static_cast<int32_t>(ki & 0x1FFFF);
-    khs[rb] = static_cast<int32_t>(ks >> 17);
-    kls[rb] = static_cast<int32_t>(ks & 0x1FFFF);
+    nki[rb] = neg_half(ci);
+    nks[rb] = neg_half(cs);
   }
 
   // ---- phase 1: scores of this wave's key tiles, kept in registers ----
   float sreg[kMaxT][4][RB];
-  uint32_t vreg[kMaxT][4];  // value scales of the same tokens, for phase 2
+  uint32_t vreg[kMaxT][4];  // value scales of the same tokens (0 outside the range), for phase 2
   float mloc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) mloc[rb] = -INFINITY;
-  float vnumax = 0.0f, vrhomax = 0.0f;
+  // largest value scales of the split: the fp16 pair (nu~, rho~) as bits, maxima
+  // per half (non-negative halves order as unsigned integers)
+  us2 vsmax = {0, 0};
+  const int nvalid = vhi - vlo;
 #pragma unroll
   for (int kt = 0; kt < kMaxT; ++kt) {
     if (kt < nk) {
@@ -587,10 +603,18 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
       wait_chunk(kt);
       const unsigned char *sl = &ring[wave][kt % kSlots][0];
       const int tile = wave + 4 * kt;
+      // Token of lane column col in block nb.  Attention: token 32 (g / 2) + 8 nb + s + 4 (g % 2)
+      // with (g, s) = (col / 4, col % 4), the slot that lands in byte nb of operand
+      // word s of lane group g of the value products, so that phase 2 can turn
+      // the lane's four weights into its operand words in registers.  Scoring:
+      // token 16 nb + col, so that a lane group's stores are 16 consecutive scores.
+      const int tok0 = SCORES ? col : 32 * (col >> 3) + 4 * ((col >> 2) & 1) + (col & 3);
+      const int tstep = SCORES ? 16 : 8;
+      const int rel = tile * 64 + tok0 - vlo;  // slot of the lane's token of block 0, from the first valid one
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const int tok = nb * 16 + col, t = tile * 64 + tok;
-        const bool valid = t >= vlo && t < vhi;
+        const int tok = tok0 + tstep * nb, t = tile * 64 + tok;
+        const bool valid = static_cast<unsigned>(rel + tstep * nb) < static_cast<unsigned>(nvalid);
         // lane group grp holds words grp, grp + 4, ... of the token's planes
         uint32_t wd[3][NW], ws[NW];
 #pragma unroll
@@ -602,7 +626,10 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
         const uint32_t ksc = lds32(sl + P::K_KS + 4 * tok), vsc = lds32(sl + P::K_VS + 4 * tok);
         v4i acc_i[RB], acc_s[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc_i[rb] = acc_s[rb] = v4i{0, 0, 0, 0};
+        for (int rb = 0; rb < RB; ++rb) {
+          acc_i[rb] = nki[rb];
+          acc_s[rb] = nks[rb];
+        }
 #pragma unroll
         for (int c = 0; c < C; ++c) {
 #pragma unroll
@@ -616,13 +643,13 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
           for (int rb = 0; rb < RB; ++rb) acc_s[rb] = mfma(qa[rb][PK][c], B, acc_s[rb]);
         }
         const float knu = f16v(ksc), krho = f16v(ksc >> 16);
-        vreg[kt][nb] = vsc;
-        vnumax = fmaxf(vnumax, valid ? f16v(vsc) : 0.0f);
-        vrhomax = fmaxf(vrhomax, valid ? f16v(vsc >> 16) : 0.0f);
+        const uint32_t vscv = valid ? vsc : 0u;
+        vreg[kt][nb] = vscv;
+        vsmax = __builtin_elementwise_max(vsmax, __builtin_bit_cast(us2, vscv));
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          const float ri = score_sum(acc_i[rb], khi[rb], kli[rb]);
-          const float rs = score_sum(acc_s[rb], khs[rb], kls[rb]);
+          const float ri = score_sum(acc_i[rb]);
+          const float rs = score_sum(acc_s[rb]);
           float sv = fmaf(knu * __int_as_float(qf[rb].x), ri, (krho * __int_as_float(qf[rb].y)) * rs);
           if (SCORES) {
             // stored at once (16 consecutive scores per row and lane group), by every
@@ -649,6 +676,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) mloc[rb] = fmaxf(mloc[rb], lane_xor_f(mloc[rb], o, lane));
+  float vnumax = f16v(vsmax.x), vrhomax = f16v(vsmax.y);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     vnumax = fmaxf(vnumax, lane_xor_f(vnumax, o, lane));
@@ -694,60 +722,47 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
       const int s = nk + r, par = AWP == 2 ? (r & 1) : 0;
       if (s + kSlots - 1 < nch) issue(s + kSlots - 1);
       if (r < nk) {
-        // weights of this wave's tile 4 r + wave (its key tile r): lane (col, grp)
-        // takes token nb 16 + col of head rb 4 + grp; its digit words go to the
-        // wave's staging block at the token's operand byte position 16 q + 4 sft + i
-        // (lane group q of the value operand, word sft, byte i): the weight's
-        // first, then the residual weight's
-        const int tile = 4 * r + wave;
-        uint32_t dres[4][RB];
+        // Weights of this wave's tile 4 r + wave (its key tile r).  Lane (col, grp)
+        // holds the scores of head 4 rb + grp for its four tokens (blocks nb), which
+        // are bytes nb of operand word s = col % 4 of lane group g = col / 4 of the
+        // value products.  Each weight becomes the four signed digits of its
+        // fixed-point value (weight, then residual weight); a 4 x 4 byte transpose
+        // gives, per digit l, the word of row (head grp, digit l) at word s of lane
+        // group g.  Rows are stored XOR-swizzled by g (row ^ g), so that the 64
+        // lanes' stores fall in distinct banks.  A token outside the range has
+        // score -inf (weight 0) and value scales 0.
+        const float s2 = ldexpf(1.0f, Ew - (col & 3)), s2p = ldexpf(1.0f, Ewp - (col & 3));
+        uint32_t dw[2][RB][4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const int w64 = nb * 16 + col, t = tile * 64 + w64;
-          const bool valid = t >= vlo && t < vhi;
-          const float vnu = valid ? f16v(vreg[r][nb]) : 0.0f, vrho = valid ? f16v(vreg[r][nb] >> 16) : 0.0f;
-          const int sft = w64 & 3, bi = (w64 >> 3) & 3, q = 2 * (w64 >> 5) + ((w64 >> 2) & 1);
-          const int pos = 16 * q + 4 * sft + bi;
-          const float sw = ldexpf(vnu, Ew - sft), swp = ldexpf(vrho, Ewp - sft);
+          const float vnu = f16v(vreg[r][nb]), vrho = f16v(vreg[r][nb] >> 16);
+          const float sw = vnu * s2, swp = vrho * s2p;  // scale 2^(E - s), exact
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            const float Pw = valid ? __builtin_amdgcn_exp2f(sreg[r][nb][rb] - mh[rb]) : 0.0f;
+            const float Pw = __builtin_amdgcn_exp2f(sreg[r][nb][rb] - mh[rb]);
             lloc[rb] += Pw;
             // truncation toward zero: |error| < 1 unit of 2^-Ew, far below the
             // 24-bit resolution of the float weight itself
-            fst[wave][rb][grp][pos] = digits(static_cast<int32_t>(Pw * sw));
-            dres[nb][rb] = digits(static_cast<int32_t>(Pw * swp));
+            dw[0][rb][nb] = digits(static_cast<int32_t>(Pw * sw));
+            dw[1][rb][nb] = digits(static_cast<int32_t>(Pw * swp));
           }
         }
-        // operand of lane (row col, group grp): row = (head, digit l); word sft
-        // gathers digit l of the four staged words 16 grp + 4 sft + (0..3)
-        const int hd = col >> 2, l = col & 3;
-        const uint32_t sel = uint32_t(l) | (uint32_t(4 + l) << 8) | 0x0C0C0000u;
+        const int g = col >> 2, sw4 = 4 * (col & 3);
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          if (x == 1) {
-            // the staged words of part 0 have been read (this wave's LDS operations
-            // complete in order): stage the residual weights in their place
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-              const int w64 = nb * 16 + col;
-              const int pos = 16 * (2 * (w64 >> 5) + ((w64 >> 2) & 1)) + 4 * (w64 & 3) + ((w64 >> 3) & 3);
-#pragma unroll
-              for (int rb = 0; rb < RB; ++rb) fst[wave][rb][grp][pos] = dres[nb][rb];
-            }
-          }
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            uint32_t wv[4];
+            const uint32_t *a4 = dw[x][rb];
+            const uint32_t t0 = __builtin_amdgcn_perm(a4[1], a4[0], 0x05010400u);  // a0.d0 a1.d0 a0.d1 a1.d1
+            const uint32_t t1 = __builtin_amdgcn_perm(a4[1], a4[0], 0x07030602u);  // a0.d2 a1.d2 a0.d3 a1.d3
+            const uint32_t t2 = __builtin_amdgcn_perm(a4[3], a4[2], 0x05010400u);
+            const uint32_t t3 = __builtin_amdgcn_perm(a4[3], a4[2], 0x07030602u);
+            const uint32_t o[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
+                                   __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
 #pragma unroll
-            for (int sv = 0; sv < 4; ++sv) {
-              const uint4 f = *reinterpret_cast<const uint4 *>(&fst[wave][rb][hd][16 * grp + 4 * sv]);
-              const uint32_t lo2 = __builtin_amdgcn_perm(f.y, f.x, sel), hi2 = __builtin_amdgcn_perm(f.w, f.z, sel);
-              wv[sv] = __builtin_amdgcn_perm(hi2, lo2, 0x05040100u);
-            }
-            *reinterpret_cast<uint4 *>(&aw[par][x][wave][grp][rb][col][0]) = uint4{wv[0], wv[1], wv[2], wv[3]};
+            for (int l = 0; l < 4; ++l)
+              *reinterpret_cast<uint32_t *>(&aw[par][x][wave][g][rb][(4 * grp + l) ^ g][sw4]) = o[l];
           }
-        }
       }
       lds_barrier();
       wait_chunk(s);
@@ -758,8 +773,8 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
         v4i aw0[RB], aw1[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          aw0[rb] = *reinterpret_cast<const v4i *>(&aw[par][0][tt][grp][rb][col][0]);
-          aw1[rb] = *reinterpret_cast<const v4i *>(&aw[par][1][tt][grp][rb][col][0]);
+          aw0[rb] = *reinterpret_cast<const v4i *>(&aw[par][0][tt][grp][rb][col ^ grp][0]);
+          aw1[rb] = *reinterpret_cast<const v4i *>(&aw[par][1][tt][grp][rb][col ^ grp][0]);
           ak[0][rb] = mfma(aw0[rb], ones, ak[0][rb]);
           ak[1][rb] = mfma(aw1[rb], ones, ak[1][rb]);
         }
@@ -1075,27 +1090,31 @@ __global__ __launch_bounds__(512) void decode_merge_grouped(DecodeArgs a, int nq
   }
 }
 
-template <int D, int RB, int BQK, bool DEEP>
+template <int D, int RB, int BQK, int SLOTS, int AWP>
 int launch_partial_bv(int bqv, const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hkv, a.batch);
   if (a.split_tokens > kMaxT * 256 || a.n_split > kMaxSplits) return 1;
   switch (bqv) {
-    case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1, DEEP>), grid, dim3(256), 0, s, a); return 0;
-    case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2, DEEP>), grid, dim3(256), 0, s, a); return 0;
-    case 3: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 3, DEEP>), grid, dim3(256), 0, s, a); return 0;
+    case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1, SLOTS, AWP>), grid, dim3(256), 0, s, a); return 0;
+    case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2, SLOTS, AWP>), grid, dim3(256), 0, s, a); return 0;
+    case 3: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 3, SLOTS, AWP>), grid, dim3(256), 0, s, a); return 0;
     default: return 1;
   }
 }
 
-template <int D, int RB, bool DEEP>
+template <int D, int RB, int SLOTS, int AWP>
 int launch_partial(const DecodeArgs &a, hipStream_t s) {
   switch (a.k.bq) {
-    case 1: return launch_partial_bv<D, RB, 1, DEEP>(a.v.bq, a, s);
-    case 2: return launch_partial_bv<D, RB, 2, DEEP>(a.v.bq, a, s);
-    case 3: return launch_partial_bv<D, RB, 3, DEEP>(a.v.bq, a, s);
+    case 1: return launch_partial_bv<D, RB, 1, SLOTS, AWP>(a.v.bq, a, s);
+    case 2: return launch_partial_bv<D, RB, 2, SLOTS, AWP>(a.v.bq, a, s);
+    case 3: return launch_partial_bv<D, RB, 3, SLOTS, AWP>(a.v.bq, a, s);
     default: return 1;
   }
 }
+
+// Ring depth of the split pass (slots per wave) for one and two row blocks of
+// heads when the grid is large, so that several work-groups share a CU.
+constexpr int kSlotsRb1 = 2, kSlotsRb2 = 2;
 
 template <int D>
 int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
@@ -1103,10 +1122,11 @@ int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
   if (nq >= 512)
     hipLaunchKernelGGL(decode_qprep_grouped<D>, dim3((nq + 7) / 8 * (2 * D / 64)), dim3(256), 0, s, a, int(nq));
   else hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
-  // one head block and at most about two work-groups per CU: the deep ring
+  // one head block and at most about two work-groups per CU: a deep ring (two
+  // chunks in flight per wave) and two operand buffers
   const bool deep = int64_t(a.n_split) * a.Hkv * a.batch <= 1024;
-  int e = rb == 2 ? launch_partial<D, 2, false>(a, s) : deep ? launch_partial<D, 1, true>(a, s)
-                                                              : launch_partial<D, 1, false>(a, s);
+  int e = rb == 2 ? launch_partial<D, 2, kSlotsRb2, 1>(a, s)
+                  : deep ? launch_partial<D, 1, 3, 2>(a, s) : launch_partial<D, 1, kSlotsRb1, 1>(a, s);
   if (e) return e;
   // few splits per head: the projection matrix is the larger read, so heads share it
   if (nq >= 512 && a.n_split <= 64)
@@ -1118,11 +1138,12 @@ int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
 
 template <int D, int RB, int BQK, bool DEEP>
 int launch_score_bq(const DecodeArgs &a, hipStream_t s) {
+  constexpr int SLOTS = DEEP ? 3 : 2, AWP = DEEP ? 2 : 1;
   // splits rounded up to a multiple of 8 (the XCD count); the extra work-groups
   // find an empty range and return
   const dim3 grid((a.n_split + 7) / 8 * 8 * a.Hkv, 1, a.batch);
   if (a.split_tokens > kMaxT * 256) return 1;
-  hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, BQK, DEEP, true>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, BQK, SLOTS, AWP, true>), grid, dim3(256), 0, s, a);
   return 0;
 }
 
