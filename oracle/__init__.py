@@ -41,9 +41,9 @@ from .quantize import quantize, quantize_conditional
 from .layout import (pack_token_major, unpack_token_major, pack_block32,
                      unpack_block32, record_bytes)
 from .dequant import dequantize
-from .attention import attention
+from .attention import attention, attention_sparse_v
 from .search import score_keys
 
 __all__ = ["build_codebook", "build_codebook_sphere", "fp16_round", "quantize", "quantize_conditional",
            "pack_token_major", "unpack_token_major", "pack_block32", "unpack_block32",
-           "record_bytes", "dequantize", "attention", "score_keys"]
+           "record_bytes", "dequantize", "attention", "attention_sparse_v", "score_keys"]
