@@ -572,6 +572,21 @@ def bench_decode_step(args, w, s, rot, proj):
     q_avg, d_avg = float(qt.mean()), float(dt_.mean())
     roof_dec = roofline_decode(w, packed_bytes, d_avg)
     q_bytes = 2 * B * H * (d * 2 + rec)
+    out_sparse = None
+    if args.sparse_v > 0:
+        out_sparse = torch.empty_like(out)
+
+        def step_sparse(i, evs=None):
+            kc, vc = caches[i % R]
+            if evs is not None:
+                evs[0].record(stream)
+                evs[1].record(stream)
+            s.decode(Q, st_d, ln_d, max_len, kc, vc, out=out_sparse, workspace=ws, stream=stream,
+                     sparse_v=args.sparse_v)
+            if evs is not None:
+                evs[2].record(stream)
+
+        _, st_, _ = timed_steps(args, step_sparse)
     res = {
         "ms_per_step": wall * 1e3, "value": packed_bytes / d_avg / 1e9,
         "config": {"workload": w.name, "batch": B, "kv_heads": H, "q_heads": w.n_q_heads,
@@ -596,6 +611,15 @@ def bench_decode_step(args, w, s, rot, proj):
 
     if not args.no_quality:
         res["quality"] = quality_report(w, rot, proj, ctx, Qn, out.cpu().numpy(), mse_only)
+    if out_sparse is not None:
+        sp = float(st_.mean())
+        res["sparse_v"] = {"tau": args.sparse_v, "decode_call_s": sp, "GBps_of_dense_bytes": packed_bytes / sp / 1e9,
+                           "speedup_vs_dense": d_avg / sp,
+                           "note": "Sparse V decode: a first pass over the keys finds each head's largest score, "
+                                   "then the split pass leaves out the values of positions with weight below tau "
+                                   "times the largest (the bytes read are the dense decode's plus the keys again)"}
+        if not args.no_quality:
+            res["sparse_v"]["quality"] = quality_vs_unquantized(w, ctx, Qn, out_sparse.cpu().numpy())
     return res
 
 
@@ -609,6 +633,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quality", action="store_true", help="skip the host-side quality report")
+    ap.add_argument("--sparse-v", type=float, default=0.0, metavar="TAU",
+                    help="also time Sparse V decode (values of positions with weight below TAU times the "
+                         "largest left out) on workloads 3 and 4")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only plain 1 GiB device copies (HBM counter calibration)")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),

@@ -222,6 +222,26 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
                         const tq_cache *kc, const tq_cache *vc, float sm_scale, float *out,
                         uint32_t *status, void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Sparse V decode attention: tq_decode_attention whose value sum leaves out
+ * the positions with low attention weight (kiosknews.app, "3 бита вместо 16:
+ * разбираем TurboQuant и когда его реально стоит включать", section "Что
+ * работает прямо сейчас и как попробовать", llama.cpp paragraph: decode skips
+ * positions with low attention weights).  The page gives no rule; reading
+ * taken: with M the head's largest score over the sequence, the value of
+ * position t is left out when exp(s_t - M) < tau; the softmax normalizer keeps
+ * every position, so out = sum over kept t of softmax(s)_t v~_t.  tau = 0 is
+ * tq_decode_attention; tau = 1 keeps only the positions of the largest score.
+ * Runs a first pass over the keys that records every split's largest score,
+ * then the split pass, which skips the value products of 64-token tiles whose
+ * values are all left out.  Same arguments, workspace and errors as
+ * tq_decode_attention, plus TQ_ERR_INVALID_ARG for tau outside [0, 1] and
+ * TQ_ERR_UNSUPPORTED for 0 < tau on shapes the matrix-core kernels do not take
+ * (d other than 128 and 256, G other than 4 and 8, asymmetric codebooks). */
+int tq_decode_attention_sparse_v(const tq_config *cfg, const void *q, tq_dtype dt, int32_t batch,
+                                 const int64_t *seq_start, const int32_t *seq_len, int32_t max_len,
+                                 const tq_cache *kc, const tq_cache *vc, float sm_scale, float tau, float *out,
+                                 uint32_t *status, void *workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Bytes of the fixed device scratch behind tq_decode_attention_noalloc (per device). */
 #define TQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 

@@ -24,7 +24,8 @@ TQ_FLAG_NONFINITE_INPUT, TQ_FLAG_SCALE_OVERFLOW, TQ_FLAG_OUT_OF_RANGE = 1, 2, 4
 TQ_MAX_LEVELS = 8
 
 EXPORTED = ("tq_build_codebook", "tq_build_codebook_sphere", "tq_prepare_bytes", "tq_prepare", "tq_quantize_kv",
-            "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_noalloc",
+            "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_sparse_v",
+            "tq_decode_attention_noalloc",
             "tq_score_workspace_bytes", "tq_score_keys", "tq_status_string")
 TQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -81,6 +82,11 @@ def _load():
                                         c_void_p, c_int32, POINTER(tq_cache), POINTER(tq_cache),
                                         c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.tq_decode_attention.restype = c_int
+    lib.tq_decode_attention_sparse_v.argtypes = [POINTER(tq_config), c_void_p, c_int, c_int32, c_void_p,
+                                                 c_void_p, c_int32, POINTER(tq_cache), POINTER(tq_cache),
+                                                 c_float, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
+                                                 c_void_p]
+    lib.tq_decode_attention_sparse_v.restype = c_int
     lib.tq_decode_attention_noalloc.argtypes = [POINTER(tq_config), c_void_p, c_int, c_int32, c_void_p,
                                                 c_void_p, c_int32, POINTER(tq_cache), POINTER(tq_cache),
                                                 c_float, c_void_p, c_void_p, c_void_p]
@@ -171,6 +177,16 @@ def tq_decode_attention(cfg: tq_config, q, dt: int, batch: int, seq_start, seq_l
                                  _ptr(status), _ptr(workspace), ws_bytes, _stream(stream))
     if st != TQ_OK:
         raise TQError(st, "tq_decode_attention")
+
+
+def tq_decode_attention_sparse_v(cfg: tq_config, q, dt: int, batch: int, seq_start, seq_len, max_len: int,
+                                 kc: tq_cache, vc: tq_cache, sm_scale: float, tau: float, out, status, workspace,
+                                 ws_bytes: int, stream=None) -> None:
+    st = LIB.tq_decode_attention_sparse_v(ctypes.byref(cfg), _ptr(q), dt, batch, _ptr(seq_start), _ptr(seq_len),
+                                          max_len, ctypes.byref(kc), ctypes.byref(vc), sm_scale, tau, _ptr(out),
+                                          _ptr(status), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != TQ_OK:
+        raise TQError(st, "tq_decode_attention_sparse_v")
 
 
 def tq_decode_attention_noalloc(cfg: tq_config, q, dt: int, batch: int, seq_start, seq_len, max_len: int,

@@ -46,7 +46,7 @@ struct DecodePlan {
   int32_t n_split;       // splits per (sequence, kv head), covering max_len + 63 slots
   int32_t fast;          // 1: matrix-core kernels; 0: reference-grade kernels
   int32_t rb;            // row blocks of 16 (= G / 4) in the matrix-core kernels
-  size_t off_qr, off_qs, off_part, off_qop, off_qconst, total;  // workspace byte offsets
+  size_t off_qr, off_qs, off_part, off_qop, off_qconst, off_smax, total;  // workspace byte offsets
   int32_t part_stride;   // floats per partial record: 2 + d + m
 };
 
@@ -129,13 +129,18 @@ struct DecodeArgs {
   float *scores;
   int64_t score_ld;
   float *score_dummy;  // 64 words that scoring lanes outside the range write instead
+  // Sparse V decode: a position's value is kept when its score (base 2) reaches the
+  // head's largest score plus sparse_thr = log2(tau); smax [batch][Hq][n_split]
+  // holds every split's largest score per head
+  float sparse_thr;
+  float *smax;
 };
 
 // Host launchers (defined in the .hip translation units).  Return hipError_t.
 int launch_quantize(int d, const QuantArgs &a, hipStream_t s);
 int launch_quantize_fast(int d, const QuantArgs &a, hipStream_t s);
 int launch_decode(int d, const DecodeArgs &a, hipStream_t s);
-int launch_decode_fast(int d, int rb, const DecodeArgs &a, hipStream_t s);
+int launch_decode_fast(int d, int rb, const DecodeArgs &a, hipStream_t s, bool sparse);
 int launch_score_fast(int d, const DecodeArgs &a, hipStream_t s);
 
 }  // namespace tq

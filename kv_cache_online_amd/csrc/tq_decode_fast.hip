@@ -417,10 +417,21 @@ struct SplitShape {
   static constexpr int AWP = AWP_;
 };
 
-// SCORES: key scoring (tq_score_keys) -- phase 1 only, over key head a.kv_fixed,
-// writing each score instead of the split's attention partial.
-template <int D, int RB, int BQK, int BQV, int SLOTS, int AWP_, bool SCORES = false>
+// Modes of the split pass:
+//   kAttend  attention partials (phase 1 scores, phase 2 values);
+//   kScores  key scoring (tq_score_keys): phase 1 only, over key head
+//            a.kv_fixed, writing each score instead of a partial;
+//   kMaxima  phase 1 only, writing each head's largest score of the split (the
+//            first pass of Sparse V decode).
+// SPARSE (kAttend only): the value sum leaves out positions whose score is below
+// the head's largest score over every split (from a kMaxima pass) plus
+// a.sparse_thr = log2(tau), and skips the value products of tiles where that
+// leaves nothing; the softmax sum keeps every position.
+constexpr int kAttend = 0, kScores = 1, kMaxima = 2;
+
+template <int D, int RB, int BQK, int BQV, int SLOTS, int AWP_, int MODE = kAttend, bool SPARSE = false>
 __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
+  constexpr bool SCORES = MODE == kScores, KEYS_ONLY = MODE != kAttend;
   using P = SplitShape<D, RB, BQK, BQV, SLOTS, AWP_>;
   constexpr int C = P::C, W = P::W, NB = P::NB, NW = P::NW, G = P::G, PK = P::PK, PV = P::PV;
   constexpr int KREC = P::KREC, KSREC = P::KSREC, VREC = P::VREC, VSREC = P::VSREC, AWP = P::AWP;
@@ -430,6 +441,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char aw[AWP][2][4][4][RB][16][16];
   __shared__ float redf[4][G];
   __shared__ float redv[4][2];
+  __shared__ int tflag[AWP][4];  // Sparse V: 1 if tile (round parity, wave) keeps any value
   __shared__ float mh_s[G];
   __shared__ float lh_s[G];
 
@@ -452,11 +464,12 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   const int bh0 = b * a.Hq + h * G;
   const int stride = 2 + 2 * D;
   if (lo >= hi) {
-    if (!SCORES && tid < G) {
+    if (MODE == kAttend && tid < G) {
       float *o = a.part + (size_t(bh0 + tid) * a.n_split + split) * stride;
       o[0] = -INFINITY;
       o[1] = 0.0f;
     }
+    if (MODE == kMaxima && tid < G) a.smax[size_t(bh0 + tid) * a.n_split + split] = -INFINITY;
     return;
   }
   const int ntile = static_cast<int>((hi - abase + 63) >> 6);
@@ -473,13 +486,13 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   const u4 rkc = make_rsrc(a.k.scl + (int64_t(hk) * kcap + abase) * 2, kslots * 4);
   const int vslots = static_cast<int>((vcap - abase) < S ? (vcap - abase) : S);
   // (scoring has no value cache: empty descriptors, whose loads return zeros)
-  const u4 rvc = SCORES ? make_rsrc(a.k.scl, 0) : make_rsrc(a.v.scl + (int64_t(h) * vcap + abase) * 2, vslots * 4);
-  const u4 rv = SCORES ? make_rsrc(a.k.idx, 0) : make_rsrc(a.v.idx + (int64_t(h) * vblocks + blk0) * BQV * D, vblk * VREC);
-  const u4 rvs = SCORES || !skv ? make_rsrc(a.k.idx, 0) : make_rsrc(a.v.sgn + (int64_t(h) * vblocks + blk0) * D, vblk * VSREC);
+  const u4 rvc = KEYS_ONLY ? make_rsrc(a.k.scl, 0) : make_rsrc(a.v.scl + (int64_t(h) * vcap + abase) * 2, vslots * 4);
+  const u4 rv = KEYS_ONLY ? make_rsrc(a.k.idx, 0) : make_rsrc(a.v.idx + (int64_t(h) * vblocks + blk0) * BQV * D, vblk * VREC);
+  const u4 rvs = KEYS_ONLY || !skv ? make_rsrc(a.k.idx, 0) : make_rsrc(a.v.sgn + (int64_t(h) * vblocks + blk0) * D, vblk * VSREC);
 
   // ---- the wave's chunk stream ----
   const int nk = ntile > wave ? (ntile - wave + 3) >> 2 : 0;  // key tiles of this wave
-  const int nr = SCORES ? 0 : (ntile + 3) >> 2;               // value rounds
+  const int nr = KEYS_ONLY ? 0 : (ntile + 3) >> 2;            // value rounds
   const int nch = nk + nr;
   // value chunk lane roles: lane -> (block, 16-byte piece) of the wave's coordinates
   const int vblkl = NW == 1 ? (lane >> 3) : (lane >> 4), vpiece = NW == 1 ? (lane & 7) : (lane & 15);
@@ -676,6 +689,17 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) mloc[rb] = fmaxf(mloc[rb], lane_xor_f(mloc[rb], o, lane));
+  if (MODE == kMaxima) {
+    if (col == 0)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) redf[wave][rb * 4 + grp] = mloc[rb];
+    wait_vm<0>();
+    lds_barrier();
+    if (tid < G)
+      a.smax[size_t(bh0 + tid) * a.n_split + split] =
+          fmaxf(fmaxf(redf[0][tid], redf[1][tid]), fmaxf(redf[2][tid], redf[3][tid]));
+    return;
+  }
   float vnumax = f16v(vsmax.x), vrhomax = f16v(vsmax.y);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -698,6 +722,20 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   float mh[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) mh[rb] = mh_s[rb * 4 + grp];
+  // Sparse V: the value of a position is kept when its score reaches the head's
+  // largest score over every split plus log2(tau)
+  float thr[RB];
+  if constexpr (SPARSE) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float *sm = a.smax + size_t(bh0 + rb * 4 + grp) * a.n_split;
+      float m = -INFINITY;
+      for (int sp = col; sp < a.n_split; sp += 16) m = fmaxf(m, sm[sp]);
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, lane_xor_f(m, o, lane));
+      thr[rb] = m + a.sparse_thr;
+    }
+  }
 
   // ---- phase 2: per round of 4 tiles, weights to digits, then value MFMAs ----
   // av[p] accumulates digit sums of weight x bit-plane p (slot PV: sign plane,
@@ -733,6 +771,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
         // score -inf (weight 0) and value scales 0.
         const float s2 = ldexpf(1.0f, Ew - (col & 3)), s2p = ldexpf(1.0f, Ewp - (col & 3));
         uint32_t dw[2][RB][4];
+        bool keep_any = false;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const float vnu = f16v(vreg[r][nb]), vrho = f16v(vreg[r][nb] >> 16);
@@ -741,11 +780,20 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
           for (int rb = 0; rb < RB; ++rb) {
             const float Pw = __builtin_amdgcn_exp2f(sreg[r][nb][rb] - mh[rb]);
             lloc[rb] += Pw;
+            float Pv = Pw;  // the weight of the position's value
+            if constexpr (SPARSE) {
+              Pv = sreg[r][nb][rb] >= thr[rb] ? Pw : 0.0f;
+              keep_any |= Pv > 0.0f;
+            }
             // truncation toward zero: |error| < 1 unit of 2^-Ew, far below the
             // 24-bit resolution of the float weight itself
-            dw[0][rb][nb] = digits(static_cast<int32_t>(Pw * sw));
-            dw[1][rb][nb] = digits(static_cast<int32_t>(Pw * swp));
+            dw[0][rb][nb] = digits(static_cast<int32_t>(Pv * sw));
+            dw[1][rb][nb] = digits(static_cast<int32_t>(Pv * swp));
           }
+        }
+        if constexpr (SPARSE) {
+          const bool any = __ballot(keep_any) != 0;
+          if (lane == 0) tflag[par][wave] = any;
         }
         const int g = col >> 2, sw4 = 4 * (col & 3);
 #pragma unroll
@@ -770,6 +818,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         if (4 * r + tt >= ntile) break;
+        if (SPARSE && !tflag[par][tt]) continue;  // every value of the tile is left out
         v4i aw0[RB], aw1[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -1090,24 +1139,26 @@ __global__ __launch_bounds__(512) void decode_merge_grouped(DecodeArgs a, int nq
   }
 }
 
-template <int D, int RB, int BQK, int SLOTS, int AWP>
+template <int D, int RB, int BQK, int SLOTS, int AWP, bool SPARSE>
 int launch_partial_bv(int bqv, const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hkv, a.batch);
   if (a.split_tokens > kMaxT * 256 || a.n_split > kMaxSplits) return 1;
+  if (SPARSE)  // first pass: every split's largest score per head
+    hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, BQK, SLOTS, AWP, kMaxima>), grid, dim3(256), 0, s, a);
   switch (bqv) {
-    case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1, SLOTS, AWP>), grid, dim3(256), 0, s, a); return 0;
-    case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2, SLOTS, AWP>), grid, dim3(256), 0, s, a); return 0;
-    case 3: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 3, SLOTS, AWP>), grid, dim3(256), 0, s, a); return 0;
+    case 1: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 1, SLOTS, AWP, kAttend, SPARSE>), grid, dim3(256), 0, s, a); return 0;
+    case 2: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 2, SLOTS, AWP, kAttend, SPARSE>), grid, dim3(256), 0, s, a); return 0;
+    case 3: hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, 3, SLOTS, AWP, kAttend, SPARSE>), grid, dim3(256), 0, s, a); return 0;
     default: return 1;
   }
 }
 
-template <int D, int RB, int SLOTS, int AWP>
+template <int D, int RB, int SLOTS, int AWP, bool SPARSE>
 int launch_partial(const DecodeArgs &a, hipStream_t s) {
   switch (a.k.bq) {
-    case 1: return launch_partial_bv<D, RB, 1, SLOTS, AWP>(a.v.bq, a, s);
-    case 2: return launch_partial_bv<D, RB, 2, SLOTS, AWP>(a.v.bq, a, s);
-    case 3: return launch_partial_bv<D, RB, 3, SLOTS, AWP>(a.v.bq, a, s);
+    case 1: return launch_partial_bv<D, RB, 1, SLOTS, AWP, SPARSE>(a.v.bq, a, s);
+    case 2: return launch_partial_bv<D, RB, 2, SLOTS, AWP, SPARSE>(a.v.bq, a, s);
+    case 3: return launch_partial_bv<D, RB, 3, SLOTS, AWP, SPARSE>(a.v.bq, a, s);
     default: return 1;
   }
 }
@@ -1117,7 +1168,7 @@ int launch_partial(const DecodeArgs &a, hipStream_t s) {
 constexpr int kSlotsRb1 = 2, kSlotsRb2 = 2;
 
 template <int D>
-int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
+int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s, bool sparse) {
   const unsigned nq = static_cast<unsigned>(a.batch * a.Hq);
   if (nq >= 512)
     hipLaunchKernelGGL(decode_qprep_grouped<D>, dim3((nq + 7) / 8 * (2 * D / 64)), dim3(256), 0, s, a, int(nq));
@@ -1125,8 +1176,13 @@ int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s) {
   // one head block and at most about two work-groups per CU: a deep ring (two
   // chunks in flight per wave) and two operand buffers
   const bool deep = int64_t(a.n_split) * a.Hkv * a.batch <= 1024;
-  int e = rb == 2 ? launch_partial<D, 2, kSlotsRb2, 1>(a, s)
-                  : deep ? launch_partial<D, 1, 3, 2>(a, s) : launch_partial<D, 1, kSlotsRb1, 1>(a, s);
+  int e;
+  if (sparse)
+    e = rb == 2 ? launch_partial<D, 2, kSlotsRb2, 1, true>(a, s)
+                : deep ? launch_partial<D, 1, 3, 2, true>(a, s) : launch_partial<D, 1, kSlotsRb1, 1, true>(a, s);
+  else
+    e = rb == 2 ? launch_partial<D, 2, kSlotsRb2, 1, false>(a, s)
+                : deep ? launch_partial<D, 1, 3, 2, false>(a, s) : launch_partial<D, 1, kSlotsRb1, 1, false>(a, s);
   if (e) return e;
   // few splits per head: the projection matrix is the larger read, so heads share it
   if (nq >= 512 && a.n_split <= 64)
@@ -1143,7 +1199,7 @@ int launch_score_bq(const DecodeArgs &a, hipStream_t s) {
   // find an empty range and return
   const dim3 grid((a.n_split + 7) / 8 * 8 * a.Hkv, 1, a.batch);
   if (a.split_tokens > kMaxT * 256) return 1;
-  hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, BQK, SLOTS, AWP, true>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_partial_fast<D, RB, BQK, BQK, SLOTS, AWP, kScores>), grid, dim3(256), 0, s, a);
   return 0;
 }
 
@@ -1181,10 +1237,10 @@ int launch_score_fast(int d, const DecodeArgs &a, hipStream_t s) {
   return hipGetLastError() != hipSuccess;
 }
 
-int launch_decode_fast(int d, int rb, const DecodeArgs &a, hipStream_t s) {
+int launch_decode_fast(int d, int rb, const DecodeArgs &a, hipStream_t s, bool sparse) {
   int e = 1;
-  if (d == 128) e = launch_fast_d<128>(rb, a, s);
-  else if (d == 256) e = launch_fast_d<256>(rb, a, s);
+  if (d == 128) e = launch_fast_d<128>(rb, a, s, sparse);
+  else if (d == 256) e = launch_fast_d<256>(rb, a, s, sparse);
   if (e) return e;
   return hipGetLastError() != hipSuccess;
 }

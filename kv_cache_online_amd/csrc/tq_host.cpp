@@ -144,6 +144,7 @@ DecodePlan decode_plan(const tq_config &cfg, int32_t batch, int32_t max_len) {
   p.off_part = o;   o = align256(o + nq * size_t(p.n_split) * p.part_stride * 4);
   p.off_qop = o;    o = align256(o + nkv * size_t(p.rb) * 5 * (cfg.d / 64) * 64 * 16);
   p.off_qconst = o; o = align256(o + nq * 4 * 8);
+  p.off_smax = o;   o = align256(o + nq * size_t(p.n_split) * 4);
   p.total = o;
   return p;
 }
@@ -431,10 +432,16 @@ size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t ma
   return tq::decode_plan(*cfg, batch, max_len).total;
 }
 
-int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_t batch,
-                        const int64_t *seq_start, const int32_t *seq_len, int32_t max_len,
-                        const tq_cache *kc, const tq_cache *vc, float sm_scale, float *out,
-                        uint32_t *status, void *workspace, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode attention, dense (tau == 0) or Sparse V (0 < tau <= 1: a position's
+// value is left out of the sum when its weight relative to the head's largest is
+// below tau).
+int decode_impl(const tq_config *cfg, const void *q, tq_dtype dt, int32_t batch, const int64_t *seq_start,
+                const int32_t *seq_len, int32_t max_len, const tq_cache *kc, const tq_cache *vc, float sm_scale,
+                float tau, float *out, uint32_t *status, void *workspace, size_t ws_bytes, hipStream_t stream) {
   int e = check_config(cfg);
   if (e) return e;
   if (dt != TQ_F32 && dt != TQ_BF16) return TQ_ERR_INVALID_ARG;
@@ -448,6 +455,7 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
   if ((e = check_cache(kc, cfg->k)) || (e = check_cache(vc, cfg->v))) return e;
   if (kc->layout != TQ_LAYOUT_TOKEN_MAJOR || vc->layout != TQ_LAYOUT_BLOCK32) return TQ_ERR_UNSUPPORTED;
   if (!(sm_scale >= 0) || !std::isfinite(sm_scale)) return TQ_ERR_INVALID_ARG;
+  if (!(tau >= 0.0f && tau <= 1.0f)) return TQ_ERR_INVALID_ARG;
   const int G = cfg->n_q_heads / cfg->n_kv_heads;
   if (G > 16) return TQ_ERR_UNSUPPORTED;
   const tq::DecodePlan p = tq::decode_plan(*cfg, batch, max_len);
@@ -493,6 +501,8 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
   a.n_split = p.n_split;
   a.qop = ws + p.off_qop;
   a.qconst = reinterpret_cast<int32_t *>(ws + p.off_qconst);
+  a.smax = reinterpret_cast<float *>(ws + p.off_smax);
+  a.sparse_thr = tau > 0.0f ? std::log2(tau) : -INFINITY;
   for (int t = 0; t < 2; ++t) {
     const tq_codebook &cb = t ? cfg->v.cb : cfg->k.cb;
     double *wc = t ? a.walsh_v : a.walsh_k;
@@ -506,9 +516,31 @@ int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_
   // the matrix-core decode expands the codebook over odd Walsh terms only, which
   // holds for an antisymmetric codebook (every Lloyd-Max codebook of a symmetric law)
   const bool fast = p.fast && cb_symmetric(a.k.cb) && cb_symmetric(a.v.cb);
-  const int rc = fast ? tq::launch_decode_fast(cfg->d, p.rb, a, stream) : tq::launch_decode(cfg->d, a, stream);
+  const bool sparse = tau > 0.0f;
+  if (sparse && !fast) return TQ_ERR_UNSUPPORTED;  // Sparse V runs on the matrix-core kernels only
+  const int rc = fast ? tq::launch_decode_fast(cfg->d, p.rb, a, stream, sparse) : tq::launch_decode(cfg->d, a, stream);
   if (rc != 0) return TQ_ERR_LAUNCH;
   return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_decode_attention(const tq_config *cfg, const void *q, tq_dtype dt, int32_t batch,
+                        const int64_t *seq_start, const int32_t *seq_len, int32_t max_len,
+                        const tq_cache *kc, const tq_cache *vc, float sm_scale, float *out,
+                        uint32_t *status, void *workspace, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(cfg, q, dt, batch, seq_start, seq_len, max_len, kc, vc, sm_scale, 0.0f, out, status,
+                     workspace, ws_bytes, stream);
+}
+
+int tq_decode_attention_sparse_v(const tq_config *cfg, const void *q, tq_dtype dt, int32_t batch,
+                                 const int64_t *seq_start, const int32_t *seq_len, int32_t max_len,
+                                 const tq_cache *kc, const tq_cache *vc, float sm_scale, float tau, float *out,
+                                 uint32_t *status, void *workspace, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(cfg, q, dt, batch, seq_start, seq_len, max_len, kc, vc, sm_scale, tau, out, status,
+                     workspace, ws_bytes, stream);
 }
 
 namespace {

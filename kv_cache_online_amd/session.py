@@ -102,7 +102,9 @@ class TQSession:
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
 
     def decode(self, q, seq_start, seq_len, max_len, kc: PackedCache, vc: PackedCache, out=None,
-               workspace=None, sm_scale=0.0, stream=None):
+               workspace=None, sm_scale=0.0, stream=None, sparse_v=0.0):
+        """Decode attention; sparse_v = tau > 0 runs Sparse V decode (values of
+        positions whose weight relative to the largest is below tau left out)."""
         batch, hq, d = q.shape
         assert hq == self.n_q_heads and d == self.d and q.is_contiguous()
         assert seq_start.dtype == torch.int64 and seq_len.dtype == torch.int32
@@ -110,9 +112,14 @@ class TQSession:
             out = torch.empty(batch, hq, d, dtype=torch.float32, device=self.device)
         if workspace is None:
             workspace = self.workspace(batch, max_len)
-        B.tq_decode_attention(self.cfg, q, self.dtype_code(q), batch, seq_start, seq_len, max_len,
-                              kc.desc, vc.desc, sm_scale, out, self.status, workspace,
-                              workspace.numel(), stream)
+        if sparse_v > 0.0:
+            B.tq_decode_attention_sparse_v(self.cfg, q, self.dtype_code(q), batch, seq_start, seq_len, max_len,
+                                           kc.desc, vc.desc, sm_scale, sparse_v, out, self.status, workspace,
+                                           workspace.numel(), stream)
+        else:
+            B.tq_decode_attention(self.cfg, q, self.dtype_code(q), batch, seq_start, seq_len, max_len,
+                                  kc.desc, vc.desc, sm_scale, out, self.status, workspace,
+                                  workspace.numel(), stream)
         return out
 
     def score_workspace(self, n_q, max_n):

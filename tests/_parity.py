@@ -177,6 +177,15 @@ def decode_reference(q64, kcache, vcache, k_bits, v_bits, k_sketch, v_sketch, ro
     q64: [G * len(kv_heads), d] queries of the query heads mapped to kv_heads (in order);
     kcache / vcache: (idx, sgn, scl) host arrays.  Returns [len(kv_heads) * G, d].
     """
+    kh, vh = dequantize_caches(kcache, vcache, k_bits, v_bits, k_sketch, v_sketch, rot, proj, cb_k, cb_v,
+                               start, length, kv_heads)
+    return O.attention(q64, kh, vh)
+
+
+def dequantize_caches(kcache, vcache, k_bits, v_bits, k_sketch, v_sketch, rot, proj, cb_k, cb_v,
+                      start, length, kv_heads):
+    """The oracle's reconstruction of the keys and values the device-written caches
+    hold for slots start .. start + length of kv_heads: ([H, T, d], [H, T, d])."""
     slots = np.arange(start, start + length)
     kh, vh = [], []
     for h in kv_heads:
@@ -186,4 +195,4 @@ def decode_reference(q64, kcache, vcache, k_bits, v_bits, k_sketch, v_sketch, ro
         i, s, nb, rb = unpack_tokens(*vcache, 1, h, slots, v_bits)
         vh.append(O.dequantize(i, s if v_sketch else None, f16(nb), f16(rb) if v_sketch else None,
                                rot, proj, cb_v))
-    return O.attention(q64, np.stack(kh), np.stack(vh))
+    return np.stack(kh), np.stack(vh)

@@ -632,3 +632,68 @@ def test_adjacent_sequences_share_blocks(wid):
     for a, b in zip(together, apart):
         np.testing.assert_array_equal(a, b)
     assert run.status() == 0
+
+
+@pytest.mark.parametrize("wid,batch,T", [(2, 2, 3000), (3, 2, 2500), (5, 2, 1500), (4, 3, 5000)])
+def test_sparse_v(wid, batch, T):
+    """Sparse V decode against the oracle's attention_sparse_v over the same packed
+    bytes, for tau from 1e-4 to 1 (only the largest scores kept).  A position whose
+    score lies within 1e-4 (natural-log units) of the keep threshold may go either
+    way, so its weight x max|v| is added to that head's 1e-4 x max|V| tolerance;
+    such positions are counted in the record.  Also: the output differs from dense
+    decode once values are left out, and equals it at a tau below every weight."""
+    w = W.WORKLOADS[wid]
+    run = Run(w, batch=batch, n_tokens=T)
+    run.quantize()
+    G = w.group
+    starts = torch.from_numpy(np.asarray(run.starts, np.int64)).cuda()
+    lens = torch.from_numpy(run.lens.astype(np.int32)).cuda()
+    kcache, vcache = run.host_caches()
+    dense = run.decode()
+    scale = 1.0 / math.sqrt(w.d)
+    recs = []
+    # a tau below every position's relative weight (from the oracle's scores), if
+    # float32 can hold it: nothing is left out
+    wmin = 1.0
+    for s in range(batch):
+        for h in range(w.n_kv_heads):
+            kh, _ = PR.dequantize_caches(kcache, vcache, run.k_bits, run.v_bits, run.k_sketch, run.v_sketch,
+                                         run.rot, run.proj, run.cb_k, run.cb_v, int(run.starts[s]),
+                                         int(run.lens[s]), [h])
+            sc = kh[0] @ W.to_f64(run.Q[s, h * G:(h + 1) * G], w.dtype).T * scale
+            wmin = min(wmin, float(np.min(np.exp(sc - sc.max(axis=0)))))
+    tau_none = 0.25 * wmin if wmin > 1e-30 else None
+    for tau in (1e-4, 1e-2, 0.3, 1.0) + ((tau_none,) if tau_none else ()):
+        out = run.s.decode(run.dev(run.Q), starts, lens, run.T, run.kc, run.vc, sparse_v=tau)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy().astype(np.float64)
+        worst, near, dropped = 0.0, 0, 0
+        for s in range(batch):
+            for h in range(w.n_kv_heads):
+                kh, vh = PR.dequantize_caches(kcache, vcache, run.k_bits, run.v_bits, run.k_sketch, run.v_sketch,
+                                              run.rot, run.proj, run.cb_k, run.cb_v, int(run.starts[s]),
+                                              int(run.lens[s]), [h])
+                q64 = W.to_f64(run.Q[s, h * G:(h + 1) * G], w.dtype)
+                ref, kept = O.attention_sparse_v(q64, kh, vh, tau, scale)
+                vmax = np.max(np.abs(W.to_f64(run.V[s, h, :int(run.lens[s])], w.dtype)))
+                for g in range(G):
+                    sc = kh[0] @ q64[g] * scale
+                    p = np.exp(sc - sc.max())
+                    p /= p.sum()
+                    band = np.abs(sc - (sc.max() + math.log(tau))) < 1e-4
+                    near += int(band.sum())
+                    dropped += int((~kept[g]).sum())
+                    tol = 1e-4 * vmax + p[band].sum() * np.abs(vh[0]).max()
+                    err = np.max(np.abs(out[s, h * G + g] - ref[g]))
+                    worst = max(worst, err / vmax)
+                    assert err <= tol, (tau, s, h, g, err, tol)
+        recs.append({"label": f"sparse-v w{wid}", "kind": "sparse decode", "tau": tau, "worst_err_over_maxV": worst,
+                     "near_threshold_positions": near, "dropped_positions": dropped})
+        if tau == tau_none:
+            assert dropped == 0
+            np.testing.assert_array_equal(out, dense)     # nothing left out: the dense result bit for bit
+        elif tau >= 1e-2:
+            assert dropped > 0 and np.max(np.abs(out - dense)) > 0
+    _record(w.name, recs)
+    _log(recs)
+    assert run.status() == 0
