@@ -51,14 +51,29 @@ METRIC = "packed-KV decode-attention GB/s (% HBM peak); KV quantize tokens/s"
 SEARCH_WORKLOAD = "search-d128-8m-b4"
 
 
-def source_hash():
+# Sources each kernel family is built from (a counter entry stays valid while they are unchanged).
+SHARED_SOURCES = ("tq_common.h", "tq_device.h", "tq_host.cpp")
+FAMILY_SOURCES = {"decode": ("tq_decode_fast.hip",) + SHARED_SOURCES,
+                  "quantize": ("tq_quantize_fast.hip",) + SHARED_SOURCES}
+
+
+def source_hash(files=None):
+    """sha256 (16 hex digits) of the library sources, or of the given csrc files."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_online_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files if files is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def kernel_family(name):
+    return "quantize" if name.startswith("quantize") else "decode"
+
+
+def family_hash(name):
+    return source_hash(FAMILY_SOURCES[kernel_family(name)])
 
 
 def packed_record_bytes(d, m, bits_mse, sketch):
@@ -69,8 +84,8 @@ def packed_record_bytes(d, m, bits_mse, sketch):
 
 def traffic_for(prefixes, workload):
     """HBM bytes per call (sum over the call's kernels, each by name prefix) from
-    the committed rocprofv3 counter runs, if they were taken on this source and
-    this workload."""
+    the committed rocprofv3 counter runs, if they were taken on this workload and
+    on the kernel family's current sources."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -78,15 +93,15 @@ def traffic_for(prefixes, workload):
         t = json.load(open(p))
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != source_hash() or workload not in t.get("workloads", {}):
+    if workload not in t.get("workloads", {}):
         return None
     ks = t["workloads"][workload].get("kernels", {})
     total = 0.0
     for pre, n in prefixes:
-        hit = [v["bytes"] for k, v in ks.items() if k.startswith(pre)]
-        if not hit:
+        hit = [v for k, v in ks.items() if k.startswith(pre)]
+        if not hit or hit[0].get("source_hash") != family_hash(pre):
             return None
-        total += n * hit[0]
+        total += n * hit[0]["bytes"]
     return total
 
 
@@ -129,18 +144,16 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_byt
     for k in fetch:
         if k in write and k.startswith(("quantize", "decode")):
             kernels[k] = {"fetch_bytes": fetch[k] * f_scale, "write_bytes": write[k] * w_scale,
-                          "bytes": fetch[k] * f_scale + write[k] * w_scale}
+                          "bytes": fetch[k] * f_scale + write[k] * w_scale, "source_hash": family_hash(k)}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     workloads = {}
-    if os.path.exists(path):   # keep the other workloads' entries taken on the same sources
+    if os.path.exists(path):   # keep the other workloads' entries (each carries its own source hash)
         try:
-            old = json.load(open(path))
-            if old.get("source_hash") == source_hash():
-                workloads = old.get("workloads", {})
+            workloads = json.load(open(path)).get("workloads", {})
         except (OSError, ValueError):
             pass
     workloads[workload] = {"kernels": kernels}
-    out = {"source_hash": source_hash(), "copy_kernel": ck, "copy_bytes": copy_bytes,
+    out = {"copy_kernel": ck, "copy_bytes": copy_bytes,
            "fetch_scale": f_scale, "write_scale": w_scale, "workloads": workloads}
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)

@@ -659,13 +659,19 @@ struct PlaneBits4 {
 
 // Row v of a 128-vector tile, 16-byte chunks 4 i + q4 (i = 0..7): four lanes
 // read 64 contiguous bytes of a row per instruction.  Zeros outside the tokens.
+// The input is read once: non-temporal loads, so that it streams through L2
+// without evicting the matrix slices every CU reads there.
 __device__ inline void load_rows_w(const QuantArgs &a, const Tile &T, int v, int q4, uint4 *r) {
   const int tok = T.t0 + v;
   if (tok >= 0 && tok < a.n_new) {
     const size_t row = (size_t(T.b) * a.H + T.h) * size_t(a.n_new) + tok;
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.t.x) + row * WD) + q4;
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.t.x) + row * WD) + q4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = p[4 * i];
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 v = __builtin_nontemporal_load(p + 4 * i);
+      r[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = make_uint4(0, 0, 0, 0);

@@ -29,7 +29,7 @@ def _counter_csv(path, counter, rows):
 def tmp_root(tmp_path, monkeypatch):
     (tmp_path / "profiles").mkdir()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "source_hash", lambda: "feedface")
+    monkeypatch.setattr(bench, "family_hash", lambda name: "feedface" + bench.kernel_family(name))
     return tmp_path
 
 
@@ -62,6 +62,8 @@ def test_traffic_scaling_and_lookup(tmp_root, monkeypatch):
     bench.write_traffic(p["f2"], p["w2"], p["cf"], p["cw"], copy_bytes=1 << 30, workload="wl-b")
     assert bench.traffic_for([("decode_partial", 1)], "wl-b") == pytest.approx(7.0 * 2048 + 1024)
     assert bench.traffic_for([("quantize", 1)], "wl-a") is not None
-    # entries taken on other kernel sources are not used
-    monkeypatch.setattr(bench, "source_hash", lambda: "0ther")
+    # entries taken on other kernel sources are not used; each family has its own hash
+    monkeypatch.setattr(bench, "family_hash", lambda name: "0ther" if name.startswith("quantize") else
+                        "feedface" + bench.kernel_family(name))
     assert bench.traffic_for([("quantize", 1)], "wl-a") is None
+    assert bench.traffic_for([("decode_partial", 1)], "wl-b") is not None
