@@ -21,7 +21,7 @@
 //    16 rows hold 4 heads; G = 8 uses two row blocks.  A score's digit sums and
 //    its +-1 correction are recombined exactly in int32 and rounded once to
 //    fp32; a value accumulator's in float64 at the end of the split.
-//  * Exact split maximum.  A split is at most 1024 slots; its scores stay in
+//  * Exact split maximum.  A split is at most 1280 slots; its scores stay in
 //    the registers of the lanes that computed them, and the value pass runs
 //    after the split's maximum is known, so the integer accumulators never need
 //    rescaling.
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq
 //
 // Scores never leave registers: the lane that scores (head, token) in phase 1
 // is the lane that turns it into a weight in phase 2.
-constexpr int kMaxT = 4;   // key tiles per wave and split: split <= 1024 slots
+constexpr int kMaxT = 5;   // key tiles per wave and split: split <= 1280 slots
 
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;

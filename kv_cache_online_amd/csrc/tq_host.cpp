@@ -122,12 +122,15 @@ DecodePlan decode_plan(const tq_config &cfg, int32_t batch, int32_t max_len) {
   p.fast = (cfg.d == 128 || cfg.d == 256) && (G == 4 || G == 8);
   p.rb = G >= 4 ? G / 4 : 1;
   // Split length: a multiple of 256 slots (4 waves x 64), sized for about 512
-  // work-groups (two per CU), at most 1024 slots (four key tiles per wave, whose
-  // scores the split pass keeps in registers).
+  // work-groups (two per CU), at most 1280 slots (five key tiles per wave, whose
+  // scores the split pass keeps in registers).  Where the grid holds many more
+  // work-groups than the chip runs at once, the longest split is the fastest:
+  // each work-group has a fixed cost (query operands, the split maximum, its
+  // partial) and the merge reads one partial per split.
   const int64_t pairs = int64_t(batch) * cfg.n_kv_heads;
   int64_t st = pairs > 0 ? (int64_t(max_len) * pairs + 511) / 512 : 256;
   st = (st + 255) / 256 * 256;
-  if (st > 1024) st = 1024;
+  if (st > 1280) st = 1280;
   if (st < 256) st = 256;
   p.split_tokens = static_cast<int32_t>(st);
   // Splits are aligned to absolute 64-slot tiles, so a sequence may start up to 63
