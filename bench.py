@@ -186,18 +186,61 @@ def quality_vs_unquantized(w, ctx, Qn, out):
             "cosine_min": float(np.min(cos))}
 
 
-def quality_report(w, rot, proj, ctx, Qn, out, decode_mse_only):
+def score_fidelity(w, sess, kc, Qn, ctx, starts, b=0):
+    """The scores the decode works from against the exact ones, for sequence b:
+    the device's inner products <q, k~> with the packed keys (tq_score_keys)
+    against float64 q.k over the stored keys, both in logit units (divided by
+    sqrt(d)), for every query head.  Reports the RMS logit error, the spread
+    (standard deviation over tokens) of the exact logits, how often the largest
+    logit stays on the same token, and the median gap between the two largest
+    exact logits.  A softmax over many tokens turns a logit error comparable to
+    that gap into a different mixture of values."""
+    import torch
+    import workloads as W
+    G, d = w.n_q_heads // w.n_kv_heads, w.d
+    err2, spread, same, gaps, n_e = 0.0, [], 0, [], 0
+    for h in range(w.n_kv_heads):
+        k = W.to_f64(ctx(b, h)[0], w.dtype)
+        q_st = Qn[b, h * G:(h + 1) * G]
+        qp = np.zeros(((G + 7) // 8 * 8, d), dtype=q_st.dtype)
+        qp[:G] = q_st
+        qd = torch.from_numpy(qp).to(sess.device)
+        qd = qd.view(torch.bfloat16) if qp.dtype == np.uint16 else qd
+        got = sess.score_keys(qd, kc, h, int(starts[b]), len(k)).cpu().numpy()[:G].astype(np.float64)
+        ref = W.to_f64(q_st, w.dtype) @ k.T
+        e = (got - ref) / math.sqrt(d)
+        err2 += float(np.sum(e * e))
+        n_e += e.size
+        lg = ref / math.sqrt(d)
+        spread.extend(lg.std(axis=1))
+        same += int(np.sum(np.argmax(got, axis=1) == np.argmax(ref, axis=1)))
+        top2 = np.sort(lg, axis=1)[:, -2:]
+        gaps.extend(top2[:, 1] - top2[:, 0])
+    return {"sequence": b, "tokens": int(len(k)), "query_heads": len(spread),
+            "logit_err_rms": math.sqrt(err2 / n_e), "logit_std_mean": float(np.mean(spread)),
+            "top1_same_frac": same / len(spread), "top2_gap_median": float(np.median(gaps))}
+
+
+def quality_report(w, rot, proj, ctx, Qn, out, decode_mse_only, sess=None, kc=None, starts=None):
     """quality_vs_unquantized for the workload's preset and, beside it, for the
     same index bits with the residual sketch off (MSE-only; decode_mse_only(session)
-    fills that session's caches the same way and returns its decode output): the
-    sketch makes the inner products unbiased at the price of variance, which the
-    softmax amplifies where the scores are spread (outlier channels)."""
+    fills that session's caches the same way and returns its decode output and key
+    cache): the sketch makes the inner products unbiased at the price of variance,
+    which the softmax amplifies where the scores are spread (outlier channels).
+    Given the preset's session, its key cache kc and the sequence starts, each
+    entry also carries score_fidelity for sequence 0."""
     from kv_cache_online_amd.session import TQSession
     rep = {"preset": quality_vs_unquantized(w, ctx, Qn, out)}
+    if sess is not None:
+        rep["preset"]["scores"] = score_fidelity(w, sess, kc, Qn, ctx, starts)
     if w.sketch:
         s2 = TQSession(w.d, w.n_kv_heads, w.n_q_heads, rot, proj, k_bits=w.bits_mse, v_bits=w.bits_mse,
                        k_sketch=0, v_sketch=0)
-        rep[f"mse_only_{w.bits_mse}bit"] = quality_vs_unquantized(w, ctx, Qn, decode_mse_only(s2))
+        out2, kc2 = decode_mse_only(s2)
+        key = f"mse_only_{w.bits_mse}bit"
+        rep[key] = quality_vs_unquantized(w, ctx, Qn, out2)
+        if sess is not None:
+            rep[key]["scores"] = score_fidelity(w, s2, kc2, Qn, ctx, starts)
     return rep
 
 
@@ -506,10 +549,11 @@ def bench_context(args, w, s, rot, proj):
     def mse_only(s2):
         kc, vc = s2.new_caches(cap)
         s2.quantize(K0, V0, dst, kc, vc)
-        return s2.decode(Q, st_d, ln_d, max_len, kc, vc).cpu().numpy()
+        return s2.decode(Q, st_d, ln_d, max_len, kc, vc).cpu().numpy(), kc
 
     if not args.no_quality:
-        res["quality"] = quality_report(w, rot, proj, ctx, Qn, out.cpu().numpy(), mse_only)
+        res["quality"] = quality_report(w, rot, proj, ctx, Qn, out.cpu().numpy(), mse_only,
+                                        sess=s, kc=caches[0][0], starts=starts)
     return res
 
 
@@ -620,10 +664,12 @@ def bench_decode_step(args, w, s, rot, proj):
     def mse_only(s2):
         kc, vc = prefill(s2)
         s2.quantize(Kd_new, Vd_new, dst_new, kc, vc)
-        return s2.decode(Q, st_d, ln_d, max_len, kc, vc).cpu().numpy()
+        return s2.decode(Q, st_d, ln_d, max_len, kc, vc).cpu().numpy(), kc
 
     if not args.no_quality:
-        res["quality"] = quality_report(w, rot, proj, ctx, Qn, out.cpu().numpy(), mse_only)
+        # the key cache of the last timed step
+        res["quality"] = quality_report(w, rot, proj, ctx, Qn, out.cpu().numpy(), mse_only, sess=s,
+                                        kc=caches[(args.steps - 1) % R][0], starts=starts)
     if out_sparse is not None:
         sp = float(st_.mean())
         res["sparse_v"] = {"tau": args.sparse_v, "decode_call_s": sp, "GBps_of_dense_bytes": packed_bytes / sp / 1e9,

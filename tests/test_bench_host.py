@@ -67,3 +67,40 @@ def test_traffic_scaling_and_lookup(tmp_root, monkeypatch):
                         "feedface" + bench.kernel_family(name))
     assert bench.traffic_for([("quantize", 1)], "wl-a") is None
     assert bench.traffic_for([("decode_partial", 1)], "wl-b") is not None
+
+
+class _ExactScores:
+    """Stand-in for a session: score_keys returns q.k over given keys (optionally
+    perturbed on one token), on the CPU."""
+
+    device = "cpu"
+
+    def __init__(self, keys, bump=None):
+        self.keys, self.bump = keys, bump
+
+    def score_keys(self, q, kc, kv_head, start, n):
+        import numpy as np
+        import torch
+        import workloads as W
+        qf = q.float().numpy().astype(np.float64)
+        s = qf @ W.to_f64(self.keys[kv_head], "bf16")[start - start:start - start + n].T
+        if self.bump is not None:
+            s[:, self.bump[0]] += self.bump[1]
+        return torch.from_numpy(s.astype(np.float32))
+
+
+def test_score_fidelity_bookkeeping():
+    """Exact scores give zero error and the same top token everywhere; a bump on the
+    top token of every head moves the RMS error by exactly bump / sqrt(d) / sqrt(n)."""
+    import math
+    import numpy as np
+    import workloads as W
+    w = W.small(W.WORKLOADS[2], batch=1, n_kv_heads=2, n_q_heads=8, seq_len=64)
+    keys = [W.kv_chunk(w, 0, 0, h, n_tokens=64) for h in range(2)]
+    Qn = W.queries(w)
+    ctx = lambda b, h: (keys[h], None)
+    r = bench.score_fidelity(w, _ExactScores(keys), None, Qn, ctx, [0])
+    assert r["logit_err_rms"] < 1e-4 * r["logit_std_mean"] and r["top1_same_frac"] == 1.0
+    assert r["query_heads"] == 8 and r["tokens"] == 64 and r["top2_gap_median"] > 0
+    r2 = bench.score_fidelity(w, _ExactScores(keys, bump=(5, 3.0)), None, Qn, ctx, [0])
+    assert abs(r2["logit_err_rms"] - 3.0 / math.sqrt(w.d) / math.sqrt(64)) < 1e-4
