@@ -925,8 +925,10 @@ constexpr int kMaxSplits = 2048;
 
 template <int D, int CPB>
 __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
-  constexpr int NT = 512, SGN = NT / (2 * D), CHS = 32;  // split groups, split loads per chunk
+  constexpr int NT = 512, SGN = NT / (2 * D), CHS = D == 128 ? 64 : 32;  // split groups, split loads per chunk
   constexpr int RPT = 2 * D / 8;                         // matrix rows per thread
+  // matrix columns loaded at the start: every group's when they fit in registers
+  constexpr int PRE = CPB * RPT <= 64 ? CPB : 1;
   __shared__ float ws_l[kMaxSplits], ls_l[kMaxSplits];
   __shared__ float red[8];
   __shared__ float accg[SGN][2 * D];
@@ -938,15 +940,16 @@ __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
   const float *base = a.part + size_t(bh) * ns * stride;
   // step 3's matrix column: rows kq + 8 i of [Pi ; S]
   const int jj = tid & 63, kq = tid >> 6;
-  float mrow[RPT];
-  auto load_rows = [&](int col) {
+  float mrow[PRE][RPT];
+  auto load_rows = [&](int g, int col) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int k = kq + 8 * i;
-      mrow[i] = k < D ? a.rot[size_t(k) * D + col] : a.proj[size_t(k - D) * D + col];
+      mrow[g][i] = k < D ? a.rot[size_t(k) * D + col] : a.proj[size_t(k - D) * D + col];
     }
   };
-  load_rows(64 * CPB * cs + jj);
+#pragma unroll
+  for (int g = 0; g < PRE; ++g) load_rows(g, 64 * (CPB * cs + g) + jj);
   // step 2's first chunk of elements
   const int e = tid % (2 * D), sg = tid / (2 * D);
   float x[CHS];
@@ -1011,16 +1014,11 @@ __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < SGN; ++g) v[i] += accg[g][kq + 8 * i];
   }
-#pragma unroll 1
-  for (int cg = 0; cg < CPB; ++cg) {
+  auto project = [&](int cg, const float (&mr)[RPT]) {
     const int col0 = 64 * (CPB * cs + cg);
-    if (cg > 0) {
-      load_rows(col0 + jj);
-      __syncthreads();  // prj of the previous group has been read
-    }
     float pj = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) pj = fmaf(mrow[i], v[i], pj);
+    for (int i = 0; i < RPT; ++i) pj = fmaf(mr[i], v[i], pj);
     prj[kq][jj] = pj;
     __syncthreads();
     if (tid < 64) {
@@ -1028,6 +1026,22 @@ __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
 #pragma unroll
       for (int g = 0; g < 8; ++g) o += prj[g][tid];
       a.out[size_t(bh) * D + col0 + tid] = l > 0.0f ? o / l : 0.0f;
+    }
+  };
+  if constexpr (PRE > 1) {
+#pragma unroll
+    for (int cg = 0; cg < CPB; ++cg) {
+      if (cg > 0) __syncthreads();  // prj of the previous group has been read
+      project(cg, mrow[cg]);
+    }
+  } else {
+#pragma unroll 1
+    for (int cg = 0; cg < CPB; ++cg) {
+      if (cg > 0) {
+        load_rows(0, 64 * (CPB * cs + cg) + jj);
+        __syncthreads();  // prj of the previous group has been read
+      }
+      project(cg, mrow[0]);
     }
   }
 }
