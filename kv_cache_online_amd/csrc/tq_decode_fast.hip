@@ -925,7 +925,9 @@ constexpr int kMaxSplits = 2048;
 
 template <int D, int CPB>
 __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
-  constexpr int NT = 512, SGN = NT / (2 * D), CHS = D == 128 ? 64 : 32;  // split groups, split loads per chunk
+  // split groups; split loads per chunk (all of a long context's splits at once where
+  // there are heads enough to fill the chip, fewer registers otherwise)
+  constexpr int NT = 512, SGN = NT / (2 * D), CHS = D == 128 && CPB > 1 ? 64 : 32;
   constexpr int RPT = 2 * D / 8;                         // matrix rows per thread
   // matrix columns loaded at the start: every group's when they fit in registers
   constexpr int PRE = CPB * RPT <= 64 ? CPB : 1;
