@@ -24,7 +24,8 @@ decode reads is not still in the 256 MB last-level cache.
 Prints one JSON line.  value = packed-KV decode-attention GB/s (algorithmic
 packed bytes read per decode / decode call time); the quantize rate (token
 positions per second, each position = K and V of every kv head) is reported
-beside it.  Kernel durations come from HIP events on the launch stream.
+beside it.  Kernel durations come from HIP events on the launch stream, created
+without the system-scope fence a default event adds (timing only).
 
 Other modes: --search (inner-product search over a 2^23-key packed index,
 tq_score_keys); --calibrate-copy and --traffic (HBM counter calibration and
@@ -103,6 +104,62 @@ def traffic_for(prefixes, workload):
             return None
         total += n * hit[0]["bytes"]
     return total
+
+
+class HipEvent:
+    """A timing event on a HIP stream, created with hipEventDisableSystemFence.
+
+    A default event makes a system-scope release when it is recorded, which
+    writes back and invalidates the caches between the kernels it separates and
+    adds its own time to the interval it measures; an event made only for timing
+    needs no such fence (the HIP runtime's own description of the flag).  Same
+    interface as torch.cuda.Event(enable_timing=True): record(stream) and
+    elapsed_time(end) in milliseconds."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            import torch
+            torch.cuda.init()
+            # the HIP runtime torch has loaded (resolved by its soname)
+            lib = ctypes.CDLL("libamdhip64.so.7")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            for f in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventElapsedTime", "hipEventDestroy"):
+                getattr(lib, f).restype = ctypes.c_int
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ev = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self._ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream=None):
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream()
+        rc = self._lib().hipEventRecord(self._ev, st.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._lib().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if self._hip is not None and getattr(self, "_ev", None) is not None and self._ev.value:
+            self._hip.hipEventDestroy(self._ev)
 
 
 def copy_calibration(nbytes=1 << 30, reps=5):
@@ -276,7 +333,7 @@ def copy_peak_gbs(nbytes=1 << 30, reps=5):
     torch.cuda.synchronize()
     best = float("inf")
     for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = HipEvent(), HipEvent()
         e0.record()
         b.copy_(a)
         e1.record()
@@ -388,7 +445,7 @@ def bench_search(args):
         for _ in range(args.warmup):
             s.score_keys(q, kc, 0, 0, N, out=out, workspace=ws, stream=stream)
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        ev = [[HipEvent() for _ in range(2)] for _ in range(args.steps)]
         for i in range(args.steps):
             ev[i][0].record(stream)
             s.score_keys(q, kc, 0, 0, N, out=out, workspace=ws, stream=stream)
@@ -432,7 +489,7 @@ def timed_steps(args, step):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[HipEvent() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):

@@ -38,6 +38,20 @@ inline PrepLayout prep_layout(int d, int m) {
   return L;
 }
 
+// ------------------------------------------------------ query operand shape --
+// The decode's score products (v_mfma_scale_f32_16x16x128_f8f6f4) take the
+// queries as fp6 (e2m3) base-16 digits, kQDigits per entry, and the key bit
+// planes as fp4 (e2m1).  A product's 16 rows are (query head, digit slot) for a
+// group of G heads: q_slots(G) = 16 / G slots per head, q_products(G) products
+// per plane and 128-coordinate chunk to hold every digit.
+constexpr int kQDigits = 6;
+constexpr int q_slots(int G) { return 16 / G; }
+constexpr int q_products(int G) { return (kQDigits + 16 / G - 1) / (16 / G); }
+// Bytes of one group's operands: 5 plane slots x d / 128 chunks x products x 64
+// lanes x 32 bytes (six used), and 64 lanes x 32 scale bytes.
+constexpr size_t q_operand_bytes(int d, int G) { return size_t(5) * (d / 128) * q_products(G) * 64 * 32; }
+constexpr size_t q_scale_bytes() { return size_t(64) * 32; }
+
 // --------------------------------------------------------------- decode plan --
 // Token splits of the decode partial pass.  The same plan sizes the workspace
 // and the launch, so both derive it from (batch, kv heads, max_len) alone.
@@ -46,7 +60,7 @@ struct DecodePlan {
   int32_t n_split;       // splits per (sequence, kv head), covering max_len + 63 slots
   int32_t fast;          // 1: matrix-core kernels; 0: reference-grade kernels
   int32_t rb;            // row blocks of 16 (= G / 4) in the matrix-core kernels
-  size_t off_qr, off_qs, off_part, off_qop, off_qconst, off_smax, total;  // workspace byte offsets
+  size_t off_qr, off_qs, off_part, off_qop, off_qscale, off_smax, total;  // workspace byte offsets
   int32_t part_stride;   // floats per partial record: 2 + d + m
 };
 
@@ -98,8 +112,12 @@ struct DecodeArgs {
   DecodeTensorArgs k, v;
   double walsh_k[4];     // key codebook Walsh coefficients, planes ordered s0, s1, s2, s0 s1 s2
   double walsh_v[4];     // value codebook, same order
-  void *qop;             // matrix-core A operands of the queries (fast path)
-  int32_t *qconst;       // [batch][Hq][8]: at 4 and 5 alpha and beta (fp32 bits) of the score digit sums
+  // query operands of the matrix-core scores, per (sequence, kv head) group of G
+  // query heads: qop [group][plane slot 5][d / 128][q_products(G)][lane 64][8
+  // words] fp6 digits (six words used), qscale [group][lane 64][32] their E8M0
+  // scale bytes, byte (plane * d / 128 + chunk) * q_products(G) + product
+  uint32_t *qop;
+  uint8_t *qscale;
   const void *q;         // [batch][Hq][d]
   int32_t dtype;
   int32_t batch, Hkv, Hq, G;
@@ -119,7 +137,7 @@ struct DecodeArgs {
   int32_t split_tokens, n_split;
   float *out;            // [batch][Hq][d]
   uint32_t *status;
-  double qbase;          // scale of the score digit sums before 2^-E: sm_scale log2(e) (decode), 1 (scores)
+  double qbase;          // scale of the scores: sm_scale log2(e) (decode, base-2 scores), 1 (raw scores)
   // key scoring (tq_score_keys): every block reads key head kv_fixed (-1: its own),
   // slots [fix_start, fix_start + fix_len) when seq_start is null, and writes raw
   // scores [Hq][score_ld] instead of attention partials

@@ -4,23 +4,25 @@
 // (ast-softpro.ru, "Технология TurboQuant и её применение с локальными LLM",
 // section 1.3).  On MI355X the vector ALU cannot keep up with HBM if every
 // query head takes its own dot products with every unpacked coordinate, so the
-// contractions of all G query heads of a kv head run as exact integer MFMAs
-// (v_mfma_i32_16x16x64_i8):
+// contractions of all G query heads of a kv head run on the matrix cores, with
+// the packed bits as operands:
 //
 //  * Bit-plane operands.  A codebook value is an odd function of the +-1
 //    bit-planes of its index (Walsh expansion: b' = 1, 2 are linear, b' = 3 adds
 //    the triple product s0 s1 s2 = 2 (b0 ^ b1 ^ b2) - 1).  With s = 2 b - 1 a
-//    dot product with a plane is 2 <v, b> - sum(v), so the MFMA only needs 0/1
-//    bits.  A packed word (shifted right by 4 for the odd nibbles) ANDed with
-//    0x01010101 << k yields four int8 operand bytes bit << k, k = 0..3; the
-//    other operand is pre-divided by 2^k.
-//  * Fixed-point slices.  Each real operand v (Walsh-weighted rotated query,
-//    sketched query, softmax weight times scale) becomes F = rint(v 2^E) with
-//    |F| < 2^30, written as four signed base-256 digits (bytes of
-//    (F + 0x808080) ^ 0x808080).  Rows of the MFMA are (query head, digit), so
-//    16 rows hold 4 heads; G = 8 uses two row blocks.  A score's digit sums and
-//    its +-1 correction are recombined exactly in int32 and rounded once to
-//    fp32; a value accumulator's in float64 at the end of the split.
+//    dot product with a plane is 2 <v, b> - sum(v), so the products only need
+//    0/1 bits.
+//  * Scores: v_mfma_scale_f32_16x16x128_f8f6f4.  A key plane word masked four
+//    ways is an fp4 (e2m1) operand of 32 coordinates (a set bit reads 0.5, 1 or
+//    2); the queries are fp6 (e2m3) base-16 digits of 24-bit block fixed-point
+//    numbers whose digit weights ride on the E8M0 block scales, so every digit
+//    of every head sums into one fp32 accumulator row per (head, slot).
+//  * Values: v_mfma_i32_16x16x64_i8, exact.  Packed value bits (a word shifted
+//    right by 0 or 4, ANDed with 0x01010101 << k) are int8 operand bytes
+//    bit << k, k = 0..3; the softmax weights times the value scales are
+//    fixed-point integers F with |F| < 2^30, written as four signed base-256
+//    digits (bytes of (F + 0x808080) ^ 0x808080), rows (query head, digit), and
+//    recombined in float64 at the end of the split.
 //  * Exact split maximum.  A split is at most 1280 slots; its scores stay in
 //    the registers of the lanes that computed them, and the value pass runs
 //    after the split's maximum is known, so the integer accumulators never need
@@ -42,6 +44,8 @@ namespace tq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
@@ -76,6 +80,30 @@ __device__ inline uint32_t plane_word(int p, uint32_t w0, uint32_t w1, uint32_t 
 }
 
 __device__ inline v4i mfma(v4i a, v4i b, v4i c) { return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0); }
+
+// fp4 (e2m1) B operand of a key plane word: dword r holds bits 4 i + r at nibble i,
+// a set bit being 1, 1, 2, 2 for r = 0..3 (nibbles 0010, 0010, 0100, 0100).
+__device__ inline v8i fp4_planes(uint32_t w) {
+  return v8i{static_cast<int>((w << 1) & 0x22222222u), static_cast<int>(w & 0x22222222u),
+             static_cast<int>(w & 0x44444444u), static_cast<int>((w >> 1) & 0x44444444u), 0, 0, 0, 0};
+}
+
+// One score product: A = six words of fp6 (e2m3) query digits, B = fp4 key bits,
+// fp32 accumulate; the A block scale is byte q & 3 of sc[q >> 2] (E8M0), the B
+// scale 1.  q is a constant once the caller's loops unroll, so the switch folds.
+template <int N>
+__device__ __forceinline__ v4f qmfma(const uint32_t (&A)[6], v8i B, v4f c, const uint32_t (&sc)[N], int q) {
+  const v8i a = {static_cast<int>(A[0]), static_cast<int>(A[1]), static_cast<int>(A[2]),
+                 static_cast<int>(A[3]), static_cast<int>(A[4]), static_cast<int>(A[5]), 0, 0};
+  const int s = static_cast<int>(sc[q >> 2]);
+  constexpr int kOne = 0x7F7F7F7F;  // E8M0 1.0 in every byte
+  switch (q & 3) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, B, c, 2, 4, 0, s, 0, kOne);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, B, c, 2, 4, 1, s, 0, kOne);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, B, c, 2, 4, 2, s, 0, kOne);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, B, c, 2, 4, 3, s, 0, kOne);
+  }
+}
 
 // sum_l 256^l c_l, exact: every digit sum is below 2^21 in magnitude (operand
 // bytes <= 8, digits <= 128, at most 2048 terms), so pairs combine in int32.
@@ -121,53 +149,109 @@ __device__ inline void clip_seq(const DecodeArgs &a, int b, int64_t *start, int6
 }
 
 // ------------------------------------------------------------- query prep ---
+// Operands of the score products.  A key plane's bits meet the query in
+// v_mfma_scale_f32_16x16x128_f8f6f4 with the bits as fp4 (e2m1) B operand and the
+// query as fp6 (e2m3) A operand:
+//
+//  * B: lane (token col, lane group g) of chunk c takes plane word 4 c + g (its
+//    32 coordinates) and masks it four ways: dword r holds bits 4 i + r at nibble
+//    i ((w << 1) & 0x22222222, w & 0x22222222, w & 0x44444444,
+//    (w >> 1) & 0x44444444), so a set bit is the fp4 value f_r = 1, 1, 2, 2.
+//    Entry e = 8 r + i of the lane's 32 (its K index 32 g + e) is coordinate
+//    32 (4 c + g) + 4 i + r.
+//  * A: lane (row m, g) holds the same 32 coordinates.  Row m is (query head hl,
+//    digit slot s), m = 4 (hl % 4) + S (hl / 4) + s with S = 16 / G slots, so the
+//    accumulator lane that holds rows 4 g' .. 4 g' + 3 holds heads g' + 4 rb.
+//    Entry e of a block of 32 carries the target T = 2 w v_j / f_r (v the
+//    rotated or sketched query, w the Walsh coefficient times the score scale,
+//    or kappa times it for the sign plane), as a 24-bit fixed-point number
+//    F = rint(T 2^E), |F| < 2^24, with E from the block's largest |T|: F's
+//    base-16 digits in
+//    sign-magnitude form are e2m3 codes (code = sign << 5 | nibble, value
+//    nibble / 8, exact), and digit l (of product l / S, slot l % S) carries the
+//    E8M0 block scale 2^(4 l + 3 - E).
+//
+// The products then sum 2 w v_j b_j over a plane's coordinates in fp32, the
+// rows of a head's slots adding up to its score; the split pass starts each
+// accumulator at minus half the operand's product with all-ones planes (the +-1
+// form 2 b - 1 of a bit) so that the sum is w <v, 2 b - 1>.  Each entry T is
+// within 2^-24 of its block's largest |T| <= 2 |w| max|v|, so each term w v_j
+// is within 2^-23 |w| max|v| and a plane's sum within 2^-16 |w| max|v| (d = 128;
+// in practice the roundings are independent and far smaller); the fp32
+// accumulation adds a few roundings of the partial sums.
+
+// Writes one lane's operand for (plane pidx or the sign plane, word wsl of the
+// slice, product i, slot s) of query head hl of group grp: item enumerates
+// them.  vals holds the slice's 64 coordinates (c0 .. c0 + 63).
+template <int D>
+__device__ void write_query_operand(const DecodeArgs &a, const float *vals, int c0, bool sgn, int npk, int grp_idx,
+                                    int hl, int item) {
+  constexpr int NW = D / 128;
+  const int G = a.G, S = 16 / G, NM = (kQDigits + S - 1) / S;
+  const int s = item % S, i = (item / S) % NM, wsl = (item / (S * NM)) & 1, pidx = item / (S * NM * 2);
+  const int w = c0 / 32 + wsl, g = w & 3, c = w >> 2;
+  const int m = 4 * (hl & 3) + S * (hl >> 2) + s, lane = 16 * g + m, l = S * i + s;
+  const double wk = sgn ? (a.k.sketch ? a.qbase * double(a.kappa) : 0.0) : a.qbase * a.walsh_k[pidx];
+  const float *v = vals + 32 * wsl;
+  auto target = [&](int e) {
+    const int r = e >> 3;
+    const double f = r < 2 ? 1.0 : 2.0;
+    return 2.0 * wk * double(v[4 * (e & 7) + r]) / f;
+  };
+  double tmax = 0.0;
+  for (int e = 0; e < 32; ++e) tmax = fmax(tmax, fabs(target(e)));
+  const int E = tmax > 0.0 ? 23 - ilogb(tmax) : 0;  // |T| 2^E < 2^24
+  uint32_t dw[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+  if (l < kQDigits) {
+    for (int e = 0; e < 32; ++e) {
+      const int64_t F = static_cast<int64_t>(rint(ldexp(target(e), E)));
+      uint32_t mag = static_cast<uint32_t>(F < 0 ? -F : F);
+      mag = mag > 0xFFFFFFu ? 0xFFFFFFu : mag;  // rint may reach 2^24
+      const uint32_t code = (F < 0 ? 32u : 0u) | ((mag >> (4 * l)) & 15u);
+      const int pos = 6 * e, k = pos >> 5, sh = pos & 31;
+      dw[k] |= code << sh;
+      if (sh > 26) dw[k + 1] |= code >> (32 - sh);
+    }
+  }
+  const int slot = sgn ? kSigPlane : pidx;
+  uint32_t *op = a.qop + ((((size_t(grp_idx) * 5 + slot) * NW + c) * NM + i) * kWave + lane) * 8;
+  *reinterpret_cast<uint4 *>(op) = uint4{dw[0], dw[1], dw[2], dw[3]};
+  *reinterpret_cast<uint2 *>(op + 4) = uint2{dw[4], dw[5]};
+  int sc = 127 + 4 * l + 3 - E;
+  sc = sc < 0 ? 0 : sc > 254 ? 254 : sc;
+  const int pslot = sgn ? npk : pidx;
+  a.qscale[(size_t(grp_idx) * kWave + lane) * 32 + (pslot * NW + c) * NM + i] = static_cast<uint8_t>(sc);
+}
+
+__device__ inline int q_items(const DecodeArgs &a, bool sgn) {
+  const int S = 16 / a.G;
+  return (sgn ? 1 : n_walsh(a.k.bq)) * 2 * ((kQDigits + S - 1) / S) * S;
+}
+
 // Block (sequence, query head, slice t) of 2 d / 64: slice t < d / 64 covers
 // coordinates 64 t .. 64 t + 63 of q_rot = Pi q (the Walsh planes' operands),
 // slice t >= d / 64 the same coordinates of q_s = S q (the sign plane's).  It
 // computes its 64 products in fp32 (about 2^-24 relative error, far inside what
 // the scores need) from the transposed matrices, so that a wave's loads are
-// contiguous, and writes this head's four rows (one per digit) of its operand
-// entries.  The fixed-point exponent of a plane must be the same in every
-// slice, so it comes from a bound every slice can compute: |(Pi q)_j| <= ||q||
-// (Pi is orthogonal) and |(S q)_i| <= max_i ||S_i|| ||q|| (the row norms of
-// S~ = S Pi^T, equal to those of S), with 2^-10 to spare for rounding.  The
-// exact corrections sum_j F_j 2^shift_j are summed by the split pass.
+// contiguous, and writes this head's rows of its operand entries.
 template <int D>
 __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
-  constexpr int C = D / 64, NSL = 2 * D / 64, KPT = D / 4;
+  constexpr int NSL = 2 * D / 64, KPT = D / 4;
   __shared__ float q[D];
   __shared__ float part[4][64];
   __shared__ float vals[64];
-  __shared__ float red[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.x / NSL, t = blockIdx.x % NSL;
   const int b = bh / a.Hq, hq = bh % a.Hq;
-  const int kvh = hq / a.G, hl = hq % a.G, rb = hl >> 2, row0 = (hl & 3) * 4;
-  const int RB = a.G / 4;
+  const int kvh = hq / a.G, hl = hq % a.G;
   const bool sgn = t >= D / 64;
-  if (sgn && !a.k.sketch) return;  // no sign plane
   const int c0 = (sgn ? t - D / 64 : t) * 64;
   // column c0 + lane of Pi^T or S^T, rows wave KPT .. wave KPT + KPT - 1
   const float *mt = (sgn ? a.projT : a.rotT) + c0 + lane + size_t(wave) * KPT * D;
   float m[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) m[i] = mt[size_t(i) * D];
-  float ss = 0.0f, smax = 0.0f;
-  for (int j = tid; j < D; j += 256) {
-    const float v = load_q(a.q, a.dtype, size_t(bh) * D + j);
-    q[j] = v;
-    ss = fmaf(v, v, ss);
-    if (sgn) smax = fmaxf(smax, a.stnorm[j]);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    ss += lane_xor_f(ss, o, lane);
-    smax = fmaxf(smax, lane_xor_f(smax, o, lane));
-  }
-  if (lane == 0) {
-    red[0][wave] = ss;
-    red[1][wave] = smax;
-  }
+  for (int j = tid; j < D; j += 256) q[j] = load_q(a.q, a.dtype, size_t(bh) * D + j);
   __syncthreads();
   float acc = 0.0f;
 #pragma unroll
@@ -175,45 +259,9 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   part[wave][lane] = acc;
   __syncthreads();
   if (tid < 64) vals[tid] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
-  const float nq = sqrtf((red[0][0] + red[0][1]) + (red[0][2] + red[0][3]));
-  const int npk = n_walsh(a.k.bq);
-  double amax = 0.0;
-  for (int p = 0; p < npk; ++p) amax = fmax(amax, fabs(a.walsh_k[p]));
-  const double scale =
-      sgn ? double(fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]))) : amax;
-  const int E = fix_exp(scale * double(nq) * (1.0 + 0x1p-10));
   __syncthreads();
-  // entry = (plane, chunk c, lane group g, digit l): 16 bytes for VGPR s, byte i.
-  // Lane group g owns plane words g, g + 4, ...; chunk c takes word g + 4 (c >> 1)
-  // and its nibble c & 1: byte i of VGPR s is coordinate 32 (g + 4 (c >> 1)) + 8 i + s + 4 (c & 1).
-  // The slice holds words c0 / 32 and c0 / 32 + 1, both nibbles: 4 (g, c) pairs.
-  uint4 *op = reinterpret_cast<uint4 *>(static_cast<unsigned char *>(a.qop) +
-                                        (size_t(b * a.Hkv + kvh) * RB + rb) * 5 * C * kWave * 16);
-  const int nplane = sgn ? 1 : npk;
-  if (tid < nplane * 16) {
-    const int l = tid & 3, hw = (tid >> 2) & 3, pidx = tid >> 4;
-    const int w = c0 / 32 + (hw >> 1), h = hw & 1, g = w & 3, c = 2 * (w >> 2) + h;
-    const float wk = sgn ? 1.0f : static_cast<float>(a.walsh_k[pidx]);
-    uint32_t wv[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int sv = 0; sv < 4; ++sv)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 32 * w + 8 * i + sv + 4 * h;
-        const int32_t F = 2 * static_cast<int32_t>(rintf(ldexpf(wk * vals[j - c0], E - 1 - sv)));
-        wv[sv] |= ((digits(F) >> (8 * l)) & 0xFFu) << (8 * i);
-      }
-    const int slot = sgn ? kSigPlane : pidx;
-    op[(size_t(slot) * C + c) * kWave + 16 * g + row0 + l] = uint4{wv[0], wv[1], wv[2], wv[3]};
-  }
-  if (tid == 0 && (t == 0 || t == D / 64)) {
-    // alpha (Walsh planes) or beta (sign plane, 0 without one): the scale of the digit sums
-    const double base = a.qbase;  // sm_scale log2(e) (scores in base 2), or 1 for raw scores
-    int32_t *qc = a.qconst + size_t(bh) * 8;
-    if (sgn) qc[5] = __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), 1 - E)));
-    else qc[4] = __float_as_int(static_cast<float>(ldexp(base, 1 - E)));
-    if (!sgn && !a.k.sketch) qc[5] = 0;
-  }
+  const int npk = n_walsh(a.k.bq);
+  if (tid < q_items(a, sgn)) write_query_operand<D>(a, vals, c0, sgn, npk, b * a.Hkv + kvh, hl, tid);
 }
 
 // Query prep for many query heads: block (group of 8 heads, slice t), the same
@@ -221,42 +269,23 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
 // matrix read once for the group.
 template <int D>
 __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq) {
-  constexpr int C = D / 64, NSL = 2 * D / 64, KPT = D / 4, HG = 8;
+  constexpr int NSL = 2 * D / 64, KPT = D / 4, HG = 8;
   __shared__ float q[HG][D];
   __shared__ float part[HG][4][64];
   __shared__ float vals[HG][64];
-  __shared__ float qn[HG];
-  __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = blockIdx.x / NSL, t = blockIdx.x % NSL;
   const bool sgn = t >= D / 64;
-  if (sgn && !a.k.sketch) return;  // no sign plane
   const int c0 = (sgn ? t - D / 64 : t) * 64;
   const float *mt = (sgn ? a.projT : a.rotT) + c0 + lane + size_t(wave) * KPT * D;
   float m[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) m[i] = mt[size_t(i) * D];
-  float smax = 0.0f;
-  if (sgn)
-    for (int j = tid; j < D; j += 256) smax = fmaxf(smax, a.stnorm[j]);
   for (int i = tid; i < HG * D; i += 256) {
     const int h = i / D, j = i % D, bh = grp * HG + h;
     q[h][j] = bh < nq ? load_q(a.q, a.dtype, size_t(bh) * D + j) : 0.0f;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) smax = fmaxf(smax, lane_xor_f(smax, o, lane));
-  if (lane == 0) red[wave] = smax;
   __syncthreads();
-  // ||q|| of heads HG / 4 wave ..
-#pragma unroll
-  for (int u = 0; u < HG / 4; ++u) {
-    const int h = HG / 4 * wave + u;
-    float ss = 0.0f;
-    for (int j = lane; j < D; j += 64) ss = fmaf(q[h][j], q[h][j], ss);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ss += lane_xor_f(ss, o, lane);
-    if (lane == 0) qn[h] = sqrtf(ss);
-  }
 #pragma unroll
   for (int h = 0; h < HG; ++h) {
     float acc = 0.0f;
@@ -269,45 +298,13 @@ __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq
     const int h = i >> 6, c = i & 63;
     vals[h][c] = (part[h][0][c] + part[h][1][c]) + (part[h][2][c] + part[h][3][c]);
   }
-  const int npk = n_walsh(a.k.bq);
-  double amax = 0.0;
-  for (int p = 0; p < npk; ++p) amax = fmax(amax, fabs(a.walsh_k[p]));
-  const double scale = sgn ? double(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))) : amax;
   __syncthreads();
-  const int nplane = sgn ? 1 : npk;
-  for (int e = tid; e < HG * nplane * 16; e += 256) {
-    const int h = e / (nplane * 16), r = e % (nplane * 16), bh = grp * HG + h;
+  const int npk = n_walsh(a.k.bq), ni = q_items(a, sgn);
+  for (int e = tid; e < HG * ni; e += 256) {
+    const int h = e / ni, bh = grp * HG + h;
     if (bh >= nq) continue;
-    const int E = fix_exp(scale * double(qn[h]) * (1.0 + 0x1p-10));
     const int b = bh / a.Hq, hq = bh % a.Hq;
-    const int kvh = hq / a.G, hl = hq % a.G, rb = hl >> 2, row0 = (hl & 3) * 4, RB = a.G / 4;
-    uint4 *op = reinterpret_cast<uint4 *>(static_cast<unsigned char *>(a.qop) +
-                                          (size_t(b * a.Hkv + kvh) * RB + rb) * 5 * C * kWave * 16);
-    const int l = r & 3, hw = (r >> 2) & 3, pidx = r >> 4;
-    const int w = c0 / 32 + (hw >> 1), hh = hw & 1, g = w & 3, c = 2 * (w >> 2) + hh;
-    const float wk = sgn ? 1.0f : static_cast<float>(a.walsh_k[pidx]);
-    uint32_t wv[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int sv = 0; sv < 4; ++sv)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 32 * w + 8 * i + sv + 4 * hh;
-        const int32_t F = 2 * static_cast<int32_t>(rintf(ldexpf(wk * vals[h][j - c0], E - 1 - sv)));
-        wv[sv] |= ((digits(F) >> (8 * l)) & 0xFFu) << (8 * i);
-      }
-    const int slot = sgn ? kSigPlane : pidx;
-    op[(size_t(slot) * C + c) * kWave + 16 * g + row0 + l] = uint4{wv[0], wv[1], wv[2], wv[3]};
-  }
-  if ((t == 0 || t == D / 64) && tid < HG) {
-    const int bh = grp * HG + tid;
-    if (bh < nq) {
-      const int E = fix_exp(scale * double(qn[tid]) * (1.0 + 0x1p-10));
-      const double base = a.qbase;  // sm_scale log2(e) (scores in base 2), or 1 for raw scores
-      int32_t *qc = a.qconst + size_t(bh) * 8;
-      if (sgn) qc[5] = __float_as_int(static_cast<float>(ldexp(base * double(a.kappa), 1 - E)));
-      else qc[4] = __float_as_int(static_cast<float>(ldexp(base, 1 - E)));
-      if (!sgn && !a.k.sketch) qc[5] = 0;
-    }
+    write_query_operand<D>(a, vals[h], c0, sgn, npk, b * a.Hkv + hq / a.G, hq % a.G, e % ni);
   }
 }
 
@@ -317,11 +314,11 @@ __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq
 // plane loops unroll without branches); the sign planes always run, with zero
 // operands when a tensor has no sketch.
 //
-// Lane roles: lane = 16 grp + col.  In a score MFMA col is the token of a
+// Lane roles: lane = 16 grp + col.  In a score product col is the token of a
 // 16-token block and grp the lane group of the contraction (coordinates); the
-// result gives lane (col, grp) the four digit sums of query head 4 rb + grp
-// for that token.  In a value MFMA col is the coordinate of a 16-coordinate
-// block and grp the token group of the contraction.
+// result gives lane (col, grp) the digit-slot sums of query heads 4 rb + grp
+// (rb < RB) for that token.  In a value MFMA col is the coordinate of a
+// 16-coordinate block and grp the token group of the contraction.
 //
 // Data movement: every wave streams its own chunks through a private ring of
 // LDS slots with buffer loads that write LDS directly (16 bytes per lane, no
@@ -388,18 +385,9 @@ __device__ inline void lds_barrier() {
 
 __device__ inline uint32_t lds32(const unsigned char *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
-// A score accumulator's four digit slots c_l, each below 2^19 in magnitude, hold
-// the +-1 form sum_l 256^l c_l (see the corrections below): the pairs
-// lo = c0 + 2^8 c1 and hi = c2 + 2^8 c3 are exact in int32, and 2^16 hi + lo is
-// rounded to fp32.
-__device__ inline float score_sum(v4i c) {
-  const int32_t lo = c.x + (c.y << 8), hi = c.z + (c.w << 8);
-  return fmaf(static_cast<float>(hi), 65536.0f, static_cast<float>(lo));
-}
-
 template <int D, int RB, int BQK, int BQV, int SLOTS_, int AWP_>
 struct SplitShape {
-  static constexpr int C = D / 64, W = D / 32, NB = D / 64, NW = D / 128, G = 4 * RB;
+  static constexpr int W = D / 32, NB = D / 64, NW = D / 128, G = 4 * RB;
   static constexpr int PK = BQK == 3 ? 4 : BQK, PV = BQV == 3 ? 4 : BQV;
   static constexpr int KREC = BQK * W * 4, KSREC = W * 4;  // key bytes per slot: planes, signs
   static constexpr int VREC = BQV * D * 4, VSREC = D * 4;  // value bytes per 32-slot block
@@ -433,7 +421,7 @@ template <int D, int RB, int BQK, int BQV, int SLOTS, int AWP_, int MODE = kAtte
 __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   constexpr bool SCORES = MODE == kScores, KEYS_ONLY = MODE != kAttend;
   using P = SplitShape<D, RB, BQK, BQV, SLOTS, AWP_>;
-  constexpr int C = P::C, W = P::W, NB = P::NB, NW = P::NW, G = P::G, PK = P::PK, PV = P::PV;
+  constexpr int W = P::W, NB = P::NB, NW = P::NW, G = P::G, PK = P::PK, PV = P::PV;
   constexpr int KREC = P::KREC, KSREC = P::KSREC, VREC = P::VREC, VSREC = P::VSREC, AWP = P::AWP;
   constexpr int kSlots = P::SLOTS;
   __shared__ __attribute__((aligned(16))) unsigned char ring[4][kSlots][P::SLOT];
@@ -545,58 +533,67 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   // the descriptors and land zeros in a free slot.)
 #pragma unroll
   for (int s = 0; s < kSlots - 1; ++s) issue(s);
-  v4i qa[RB][PK + 1][C];
-  int2 qf[RB];  // per head: alpha and beta (fp32 bits)
+  // Query operands of the score products (fp6 digits, six words per lane) and
+  // their scale bytes, byte q = (plane (PK: sign) * NW + chunk) * NM + product.
+  constexpr int QS = 16 / G, NM = (kQDigits + QS - 1) / QS, NQB = (PK + 1) * NW * NM, NQW = (NQB + 3) / 4;
+  uint32_t qa[PK + 1][NW][NM][6];
+  uint32_t qsc[NQW];
   {
-    const v4i *qop = static_cast<const v4i *>(a.qop) + size_t(b * a.Hkv + h) * RB * 5 * C * kWave;
+    const uint32_t *qop = a.qop + size_t(b * a.Hkv + h) * 5 * NW * NM * kWave * 8;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int p = 0; p <= PK; ++p) {
+      const int slot = p == PK ? kSigPlane : p;
 #pragma unroll
-      for (int p = 0; p <= PK; ++p) {
-        const int slot = p == PK ? kSigPlane : p;
+      for (int c = 0; c < NW; ++c)
 #pragma unroll
-        for (int c = 0; c < C; ++c)
-          qa[rb][p][c] = (p < PK || skk) ? qop[((size_t(rb) * 5 + slot) * C + c) * kWave + lane] : v4i{0, 0, 0, 0};
-      }
-      qf[rb] = *reinterpret_cast<const int2 *>(a.qconst + size_t(bh0 + rb * 4 + grp) * 8 + 4);
+        for (int i = 0; i < NM; ++i) {
+          const uint32_t *src = qop + (((size_t(slot) * NW + c) * NM + i) * kWave + lane) * 8;
+          const uint4 x = *reinterpret_cast<const uint4 *>(src);
+          const uint2 y = *reinterpret_cast<const uint2 *>(src + 4);
+          qa[p][c][i][0] = x.x;
+          qa[p][c][i][1] = x.y;
+          qa[p][c][i][2] = x.z;
+          qa[p][c][i][3] = x.w;
+          qa[p][c][i][4] = y.x;
+          qa[p][c][i][5] = y.y;
+        }
     }
+    const uint32_t *qs = reinterpret_cast<const uint32_t *>(a.qscale + (size_t(b * a.Hkv + h) * kWave + lane) * 32);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int k = 0; k < NQW; ++k) qsc[k] = qs[k];
 #pragma unroll
-      for (int p = 0; p <= PK; ++p)
+    for (int p = 0; p <= PK; ++p)
 #pragma unroll
-        for (int c = 0; c < C; ++c)
-          asm volatile("" ::"v"(qa[rb][p][c].x), "v"(qa[rb][p][c].y), "v"(qa[rb][p][c].z), "v"(qa[rb][p][c].w));
-      asm volatile("" ::"v"(qf[rb].x), "v"(qf[rb].y));
-    }
+      for (int c = 0; c < NW; ++c)
+#pragma unroll
+        for (int i = 0; i < NM; ++i)
+#pragma unroll
+          for (int k = 0; k < 6; ++k) asm volatile("" ::"v"(qa[p][c][i][k]));
+#pragma unroll
+    for (int k = 0; k < NQW; ++k) asm volatile("" ::"v"(qsc[k]));
   }
+  // value products: bit-plane operand bytes (bit << k) and the all-ones plane
   const uint32_t msk[4] = {0x01010101u, 0x02020202u, 0x04040404u, 0x08080808u};
   const v4i ones = {static_cast<int>(msk[0]), static_cast<int>(msk[1]), static_cast<int>(msk[2]),
                     static_cast<int>(msk[3])};
-  // The query operands are even integers G_j = 2 F_j, so the plane products sum
-  // to x = sum_j G_j b_j 2^shift_j = 2 sum_j F_j b_j 2^shift_j.  The +-1
-  // correction k = sum_j F_j 2^shift_j, exactly half the operands' digit sums
-  // against all-ones planes (index planes summed; sign plane), is loaded into
-  // every score accumulator as -k, spread over the four digit slots (three
-  // bytes and the rest), so each slot ends at a sum below 2^19 whose weighted
-  // total sum_l 256^l c_l is the +-1 form x - k.
-  v4i nki[RB], nks[RB];
-  auto neg_half = [](v4i c) {
-    const int64_t k = (int64_t(c.x) + (int64_t(c.y) << 8) + (int64_t(c.z) << 16) + (int64_t(c.w) << 24)) >> 1;
-    return v4i{-static_cast<int>(k & 0xFF), -static_cast<int>((k >> 8) & 0xFF), -static_cast<int>((k >> 16) & 0xFF),
-               -static_cast<int>(k >> 24)};
-  };
+  // The products sum T b over a plane, with T = 2 w v / f and the bit's fp4 value
+  // f, i.e. 2 sum_j w v_j b_j.  The +-1 form needs minus sum_j w v_j, half the
+  // operand's product with all-ones planes (B = the four masks themselves),
+  // which starts every score accumulator, row by row.
+  v4f nki = {0.0f, 0.0f, 0.0f, 0.0f}, nks = {0.0f, 0.0f, 0.0f, 0.0f};
+  {
+    const v8i all = fp4_planes(0xFFFFFFFFu);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    v4i ci = {0, 0, 0, 0}, cs = {0, 0, 0, 0};
+    for (int c = 0; c < NW; ++c) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
+      for (int p = 0; p < PK; ++p)
 #pragma unroll
-      for (int p = 0; p < PK; ++p) ci = mfma(qa[rb][p][c], ones, ci);
-      cs = mfma(qa[rb][PK][c], ones, cs);
+        for (int i = 0; i < NM; ++i) nki = qmfma(qa[p][c][i], all, nki, qsc, (p * NW + c) * NM + i);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) nks = qmfma(qa[PK][c][i], all, nks, qsc, (PK * NW + c) * NM + i);
     }
-    nki[rb] = neg_half(ci);
-    nks[rb] = neg_half(cs);
+    nki *= -0.5f;
+    nks *= -0.5f;
   }
 
   // ---- phase 1: scores of this wave's key tiles, kept in registers ----
@@ -637,23 +634,18 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
           ws[u] = lds32(sl + P::K_SG + tok * KSREC + (grp + 4 * u) * 4);
         }
         const uint32_t ksc = lds32(sl + P::K_KS + 4 * tok), vsc = lds32(sl + P::K_VS + 4 * tok);
-        v4i acc_i[RB], acc_s[RB];
+        v4f acc_i = nki, acc_s = nks;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          acc_i[rb] = nki[rb];
-          acc_s[rb] = nks[rb];
-        }
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
+        for (int c = 0; c < NW; ++c) {
 #pragma unroll
           for (int p = 0; p < PK; ++p) {
-            const v4i B = expand(plane_word<4>(p, wd[0][c >> 1], wd[1][c >> 1], wd[2][c >> 1]), 4u * (c & 1), msk);
+            const v8i B = fp4_planes(plane_word<4>(p, wd[0][c], wd[1][c], wd[2][c]));
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) acc_i[rb] = mfma(qa[rb][p][c], B, acc_i[rb]);
+            for (int i = 0; i < NM; ++i) acc_i = qmfma(qa[p][c][i], B, acc_i, qsc, (p * NW + c) * NM + i);
           }
-          const v4i B = expand(ws[c >> 1], 4u * (c & 1), msk);
+          const v8i B = fp4_planes(ws[c]);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc_s[rb] = mfma(qa[rb][PK][c], B, acc_s[rb]);
+          for (int i = 0; i < NM; ++i) acc_s = qmfma(qa[PK][c][i], B, acc_s, qsc, (PK * NW + c) * NM + i);
         }
         const float knu = f16v(ksc), krho = f16v(ksc >> 16);
         const uint32_t vscv = valid ? vsc : 0u;
@@ -661,9 +653,14 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
         vsmax = __builtin_elementwise_max(vsmax, __builtin_bit_cast(us2, vscv));
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          const float ri = score_sum(acc_i[rb]);
-          const float rs = score_sum(acc_s[rb]);
-          float sv = fmaf(knu * __int_as_float(qf[rb].x), ri, (krho * __int_as_float(qf[rb].y)) * rs);
+          // rows QS rb .. QS rb + QS - 1 of this lane: the digit slots of head 4 rb + grp
+          float ri = acc_i[QS * rb], rs = acc_s[QS * rb];
+#pragma unroll
+          for (int u = 1; u < QS; ++u) {
+            ri += acc_i[QS * rb + u];
+            rs += acc_s[QS * rb + u];
+          }
+          float sv = fmaf(knu, ri, krho * rs);
           if (SCORES) {
             // stored at once (16 consecutive scores per row and lane group), by every
             // lane: a slot outside the range writes a per-lane dummy word instead, so

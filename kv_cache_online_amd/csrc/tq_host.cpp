@@ -145,8 +145,8 @@ DecodePlan decode_plan(const tq_config &cfg, int32_t batch, int32_t max_len) {
   p.off_qr = o;     o = align256(o + nq * cfg.d * 4);
   p.off_qs = o;     o = align256(o + nq * cfg.m * 4);
   p.off_part = o;   o = align256(o + nq * size_t(p.n_split) * p.part_stride * 4);
-  p.off_qop = o;    o = align256(o + nkv * size_t(p.rb) * 5 * (cfg.d / 64) * 64 * 16);
-  p.off_qconst = o; o = align256(o + nq * 4 * 8);
+  p.off_qop = o;    o = align256(o + nkv * q_operand_bytes(cfg.d, G >= 1 && G <= 16 ? G : 16));
+  p.off_qscale = o; o = align256(o + nkv * q_scale_bytes());
   p.off_smax = o;   o = align256(o + nq * size_t(p.n_split) * 4);
   p.total = o;
   return p;
@@ -502,8 +502,8 @@ int decode_impl(const tq_config *cfg, const void *q, tq_dtype dt, int32_t batch,
   a.part = reinterpret_cast<float *>(ws + p.off_part);
   a.split_tokens = p.split_tokens;
   a.n_split = p.n_split;
-  a.qop = ws + p.off_qop;
-  a.qconst = reinterpret_cast<int32_t *>(ws + p.off_qconst);
+  a.qop = reinterpret_cast<uint32_t *>(ws + p.off_qop);
+  a.qscale = ws + p.off_qscale;
   a.smax = reinterpret_cast<float *>(ws + p.off_smax);
   a.sparse_thr = tau > 0.0f ? std::log2(tau) : -INFINITY;
   for (int t = 0; t < 2; ++t) {
@@ -553,11 +553,10 @@ namespace {
 int32_t score_group(const tq_config &cfg, int32_t n_q) { return cfg.d == 128 && n_q % 16 == 0 ? 16 : 8; }
 
 // Workspace of tq_score_keys: the query operands and constants of n_q queries,
-// and 64 words that scoring lanes outside the key range write instead
-// (the operand bytes per query do not depend on the group size).
+// and 64 words that scoring lanes outside the key range write instead.
 struct ScorePlan {
   int32_t group, split_tokens, n_split;
-  size_t off_qop, off_qconst, off_dummy, total;
+  size_t off_qop, off_qscale, off_dummy, total;
 };
 
 ScorePlan score_plan(const tq_config &cfg, int32_t n_q, int32_t max_n) {
@@ -572,8 +571,8 @@ ScorePlan score_plan(const tq_config &cfg, int32_t n_q, int32_t max_n) {
   p.n_split = static_cast<int32_t>((int64_t(max_n) + 63 + st - 1) / st);
   if (p.n_split < 1) p.n_split = 1;
   size_t o = 0;
-  p.off_qop = o;    o = tq::align256(o + size_t(n_q / 4) * 5 * (cfg.d / 64) * 64 * 16);
-  p.off_qconst = o; o = tq::align256(o + size_t(n_q) * 4 * 8);
+  p.off_qop = o;    o = tq::align256(o + size_t(groups) * tq::q_operand_bytes(cfg.d, p.group));
+  p.off_qscale = o; o = tq::align256(o + size_t(groups) * tq::q_scale_bytes());
   p.off_dummy = o;  o = tq::align256(o + 64 * 4);
   p.total = o;
   return p;
@@ -642,8 +641,8 @@ int tq_score_keys(const tq_config *cfg, const void *q, tq_dtype dt, int32_t n_q,
   a.stnorm = reinterpret_cast<const float *>(prep + L.stnorm);
   a.split_tokens = p.split_tokens;
   a.n_split = p.n_split;
-  a.qop = ws + p.off_qop;
-  a.qconst = reinterpret_cast<int32_t *>(ws + p.off_qconst);
+  a.qop = reinterpret_cast<uint32_t *>(ws + p.off_qop);
+  a.qscale = ws + p.off_qscale;
   a.scores = scores;
   a.score_ld = n;
   a.score_dummy = reinterpret_cast<float *>(ws + p.off_dummy);

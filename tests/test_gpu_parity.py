@@ -511,8 +511,12 @@ def test_workspace_contents_do_not_matter(wid, batch, T):
 
 
 def test_score_symmetries():
-    """Search scores are exact linear functions of the query digits: 2q gives exactly
-    twice the scores and -q exactly their negation (checked without the oracle)."""
+    """Search scores are linear in the query operands (checked without the oracle):
+    2q scales every digit block by an exact power of two, so it gives exactly twice
+    the scores; -q negates every digit, so it negates the scores up to the matrix
+    core's fp32 accumulation, whose roundings are not sign-symmetric (a few units
+    in the last place of the partial sums; the bound allows 2^-16 of the row's
+    largest score)."""
     w = W.WORKLOADS[2]
     run = Run(w, batch=1, n_tokens=1500)
     run.quantize()
@@ -527,7 +531,11 @@ def test_score_symmetries():
 
     s1 = sc(q)
     np.testing.assert_array_equal(sc(dbl), 2 * s1)
-    np.testing.assert_array_equal(sc(q ^ np.uint16(0x8000)), -s1)
+    neg = sc(q ^ np.uint16(0x8000))
+    tol = 2.0 ** -16 * np.abs(s1).max(axis=1, keepdims=True)
+    _log({"label": "score negation", "max_abs_diff": float(np.abs(neg + s1).max()),
+          "worst_diff_over_tol": float(np.max(np.abs(neg + s1) / tol))})
+    assert np.all(np.abs(neg + s1) <= tol)
     assert run.status() == 0
 
 
