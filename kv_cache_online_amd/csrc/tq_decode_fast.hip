@@ -192,22 +192,25 @@ __device__ void write_query_operand(const DecodeArgs &a, const float *vals, int 
   const int w = c0 / 32 + wsl, g = w & 3, c = w >> 2;
   const int m = 4 * (hl & 3) + S * (hl >> 2) + s, lane = 16 * g + m, l = S * i + s;
   const double wk = sgn ? (a.k.sketch ? a.qbase * double(a.kappa) : 0.0) : a.qbase * a.walsh_k[pidx];
+  // targets T = (2 w / f) v in fp32: f = 1 for e >> 3 < 2, else 2
+  const float w1 = static_cast<float>(2.0 * wk), w2 = static_cast<float>(wk);
   const float *v = vals + 32 * wsl;
-  auto target = [&](int e) {
-    const int r = e >> 3;
-    const double f = r < 2 ? 1.0 : 2.0;
-    return 2.0 * wk * double(v[4 * (e & 7) + r]) / f;
-  };
-  double tmax = 0.0;
-  for (int e = 0; e < 32; ++e) tmax = fmax(tmax, fabs(target(e)));
-  const int E = tmax > 0.0 ? 23 - ilogb(tmax) : 0;  // |T| 2^E < 2^24
+  float t[32];
+  float tmax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    t[e] = ((e >> 3) < 2 ? w1 : w2) * v[4 * (e & 7) + (e >> 3)];
+    tmax = fmaxf(tmax, fabsf(t[e]));
+  }
+  const int E = tmax > 0.0f ? 23 - ilogbf(tmax) : 0;  // |T| 2^E < 2^24
   uint32_t dw[6] = {0u, 0u, 0u, 0u, 0u, 0u};
   if (l < kQDigits) {
+#pragma unroll
     for (int e = 0; e < 32; ++e) {
-      const int64_t F = static_cast<int64_t>(rint(ldexp(target(e), E)));
-      uint32_t mag = static_cast<uint32_t>(F < 0 ? -F : F);
+      const float F = rintf(ldexpf(t[e], E));  // an integer below 2^24 in magnitude (exact in fp32)
+      uint32_t mag = static_cast<uint32_t>(fabsf(F));
       mag = mag > 0xFFFFFFu ? 0xFFFFFFu : mag;  // rint may reach 2^24
-      const uint32_t code = (F < 0 ? 32u : 0u) | ((mag >> (4 * l)) & 15u);
+      const uint32_t code = (F < 0.0f ? 32u : 0u) | ((mag >> (4 * l)) & 15u);
       const int pos = 6 * e, k = pos >> 5, sh = pos & 31;
       dw[k] |= code << sh;
       if (sh > 26) dw[k + 1] |= code >> (32 - sh);
