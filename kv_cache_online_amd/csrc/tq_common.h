@@ -87,7 +87,10 @@ struct QuantTensorArgs {
 };
 
 struct QuantArgs {
-  QuantTensorArgs t;
+  // t, and t2 when n_tensor == 2: tensors with the same spec (b', sketch,
+  // codebook) quantized by one launch, whose tiles run over t's then t2's
+  QuantTensorArgs t, t2;
+  int32_t n_tensor;
   int32_t dtype;         // tq_dtype
   int32_t batch, H, n_new;
   const int64_t *dst;

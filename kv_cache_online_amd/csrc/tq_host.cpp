@@ -396,34 +396,53 @@ int tq_quantize_kv(const tq_config *cfg, const void *k, const void *v, tq_dtype 
   const tq::PrepLayout L = tq::prep_layout(cfg->d, cfg->m);
   const auto *prep = static_cast<const unsigned char *>(cfg->prep);
   const size_t per_tensor = size_t(batch) * cfg->n_kv_heads * n_new * 2;
-  for (int t = 0; t < 2; ++t) {
-    const void *x = t ? v : k;
-    if (!x) continue;
+  auto tensor_args = [&](int t) {
     const tq_cache *c = t ? vc : kc;
     const tq_tensor_spec &s = t ? cfg->v : cfg->k;
-    tq::QuantArgs a{};
-    a.t.x = x;
-    a.t.idx = c->idx;
-    a.t.sgn = c->sgn;
-    a.t.scl = c->scl;
-    a.t.cap = c->capacity;
-    a.t.layout = c->layout;
-    a.t.bq = s.bits_mse;
-    a.t.sketch = s.sketch;
-    a.t.cb = cb_f32(s.cb);
-    a.t.dbg = dbg_scales ? dbg_scales + t * per_tensor : nullptr;
-    a.dtype = dt;
-    a.batch = batch;
-    a.H = cfg->n_kv_heads;
-    a.n_new = n_new;
-    a.dst = dst_token;
-    a.rotT = reinterpret_cast<const float *>(prep + L.rotT);
-    a.stT = reinterpret_cast<const float *>(prep + L.stT);
-    a.rot_hml = reinterpret_cast<const uint16_t *>(prep + L.rot_hml);
-    a.st_hml = reinterpret_cast<const uint16_t *>(prep + L.st_hml);
-    a.status = status;
-    const bool fast = (cfg->d == 128 || (cfg->d == 256 && dt == TQ_BF16)) && cb_symmetric(a.t.cb);
-    const int rc = fast ? tq::launch_quantize_fast(cfg->d, a, stream) : tq::launch_quantize(cfg->d, a, stream);
+    tq::QuantTensorArgs ta{};
+    ta.x = t ? v : k;
+    ta.idx = c->idx;
+    ta.sgn = c->sgn;
+    ta.scl = c->scl;
+    ta.cap = c->capacity;
+    ta.layout = c->layout;
+    ta.bq = s.bits_mse;
+    ta.sketch = s.sketch;
+    ta.cb = cb_f32(s.cb);
+    ta.dbg = dbg_scales ? dbg_scales + t * per_tensor : nullptr;
+    return ta;
+  };
+  auto fast_ok = [&](const tq::QuantTensorArgs &ta) {
+    return (cfg->d == 128 || (cfg->d == 256 && dt == TQ_BF16)) && cb_symmetric(ta.cb);
+  };
+  tq::QuantArgs a{};
+  a.dtype = dt;
+  a.batch = batch;
+  a.H = cfg->n_kv_heads;
+  a.n_new = n_new;
+  a.dst = dst_token;
+  a.rotT = reinterpret_cast<const float *>(prep + L.rotT);
+  a.stT = reinterpret_cast<const float *>(prep + L.stT);
+  a.rot_hml = reinterpret_cast<const uint16_t *>(prep + L.rot_hml);
+  a.st_hml = reinterpret_cast<const uint16_t *>(prep + L.st_hml);
+  a.status = status;
+  a.n_tensor = 1;
+  if (k && v) {
+    // K and V with one spec (bits, sketch, codebook) share one launch of the
+    // matrix-core kernel: its set-up (the matrices into registers) is paid once
+    const tq::QuantTensorArgs tk = tensor_args(0), tv = tensor_args(1);
+    if (fast_ok(tk) && tk.bq == tv.bq && tk.sketch == tv.sketch &&
+        std::memcmp(&tk.cb, &tv.cb, sizeof(tk.cb)) == 0) {
+      a.t = tk;
+      a.t2 = tv;
+      a.n_tensor = 2;
+      return tq::launch_quantize_fast(cfg->d, a, stream) != 0 ? TQ_ERR_LAUNCH : TQ_OK;
+    }
+  }
+  for (int t = 0; t < 2; ++t) {
+    if (!(t ? v : k)) continue;
+    a.t = tensor_args(t);
+    const int rc = fast_ok(a.t) ? tq::launch_quantize_fast(cfg->d, a, stream) : tq::launch_quantize(cfg->d, a, stream);
     if (rc != 0) return TQ_ERR_LAUNCH;
   }
   return TQ_OK;

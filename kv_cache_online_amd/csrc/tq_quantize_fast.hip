@@ -68,6 +68,7 @@ struct QSmem {
 
 struct Tile {
   int b, h;
+  int tensor;     // 0: QuantArgs::t, 1: QuantArgs::t2
   int t0;         // token of row 0 (negative when the tile starts before the first token)
   int64_t base;   // slot of row 0, a multiple of 32
 };
@@ -94,11 +95,14 @@ __device__ inline int64_t load_uniform(const int64_t *p) {
   return *reinterpret_cast<const __attribute__((address_space(4))) int64_t *>(reinterpret_cast<uintptr_t>(p));
 }
 
-// Tile `tile` of TT vectors: tiles run over (sequence, head, k), and tile k of a
-// sequence starts at the 32-slot boundary at or below its first slot, plus TT k.
+// Tile `tile` of TT vectors: tiles run over (tensor, sequence, head, k), n1 per
+// tensor, and tile k of a sequence starts at the 32-slot boundary at or below its
+// first slot, plus TT k.
 template <int TT>
-__device__ inline Tile tile_at(const QuantArgs &a, uint32_t tile, FastDiv ftpb, FastDiv fh) {
+__device__ inline Tile tile_at(const QuantArgs &a, uint32_t tile, uint32_t n1, FastDiv ftpb, FastDiv fh) {
   Tile T;
+  T.tensor = tile >= n1 ? 1 : 0;
+  if (T.tensor) tile -= n1;
   const uint32_t bh = fdiv(tile, ftpb);
   const int k = static_cast<int>(tile - bh * ftpb.d);
   T.b = static_cast<int>(fdiv(bh, fh));
@@ -117,8 +121,9 @@ __device__ inline void load_rows(const QuantArgs &a, const Tile &T, int v, int c
   const int tok = T.t0 + v;
   if (tok >= 0 && tok < a.n_new) {
     const size_t row = (size_t(T.b) * a.H + T.h) * size_t(a.n_new) + tok;
-    const uint4 *p = F32 ? reinterpret_cast<const uint4 *>(static_cast<const float *>(a.t.x) + row * QD + 16 * c16)
-                         : reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.t.x) + row * QD + 16 * c16);
+    const void *x = T.tensor ? a.t2.x : a.t.x;
+    const uint4 *p = F32 ? reinterpret_cast<const uint4 *>(static_cast<const float *>(x) + row * QD + 16 * c16)
+                         : reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + row * QD + 16 * c16);
 #pragma unroll
     for (int i = 0; i < NV; ++i) r[i] = p[i];
   } else {
@@ -207,7 +212,7 @@ struct PlaneBits {
 };
 
 template <int BQ, bool F32>
-__global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_tiles, FastDiv ftpb, FastDiv fh) {
+__global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_tiles, uint32_t n1, FastDiv ftpb, FastDiv fh) {
   constexpr int NPX = F32 ? 3 : 1;
   constexpr int NV = F32 ? 4 : 2;
   constexpr int L = 1 << BQ;
@@ -262,17 +267,18 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
   uint32_t tile = blockIdx.x;
   Tile T{};
   if (tile < n_tiles) {
-    T = tile_at<QT>(a, tile, ftpb, fh);
+    T = tile_at<QT>(a, tile, n1, ftpb, fh);
     load_rows<F32>(a, T, v, c16, xr);
   }
   for (; tile < n_tiles; tile += gridDim.x) {
     const Tile cur = T;
+    const QuantTensorArgs &tt = cur.tensor ? a.t2 : a.t;  // this tile's tensor
     uint4 xc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) xc[i] = xr[i];
     const uint32_t nxt = tile + gridDim.x;
     if (nxt < n_tiles) {
-      T = tile_at<QT>(a, nxt, ftpb, fh);
+      T = tile_at<QT>(a, nxt, n1, ftpb, fh);
       load_rows<F32>(a, T, v, c16, xr);
     }
     if (cur.t0 >= a.n_new) continue;  // no token falls in this tile (uniform)
@@ -347,7 +353,7 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
         if (tok >= 0 && tok < a.n_new) {
           if (nonfinite) flags |= TQ_FLAG_NONFINITE_INPUT;
           if (over) flags |= TQ_FLAG_SCALE_OVERFLOW;
-          if (a.t.dbg) a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2] = nu;
+          if (tt.dbg) tt.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2] = nu;
         }
       }
     }
@@ -495,13 +501,13 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
           const int tok = cur.t0 + t;
           if (tok >= 0 && tok < a.n_new) {
             if (over) flags |= TQ_FLAG_SCALE_OVERFLOW;
-            if (a.t.dbg) a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = rho;
+            if (tt.dbg) tt.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = rho;
           }
         }
       } else if (t < QT) {
         const int tok = cur.t0 + t;
-        if (tok >= 0 && tok < a.n_new && a.t.dbg)
-          a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = 0.0f;
+        if (tok >= 0 && tok < a.n_new && tt.dbg)
+          tt.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = 0.0f;
       }
       if (t < QT) sm.scl[t] = sm.nub[t] | (rbits << 16);
     }
@@ -509,7 +515,7 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
 
     // ---------------------------------------------------------------- E --
     {
-      const bool in_range = cur.base >= 0 && cur.base < a.t.cap;  // base and cap are multiples of 32
+      const bool in_range = cur.base >= 0 && cur.base < tt.cap;  // base and cap are multiples of 32
       const int lo = cur.t0 < 0 ? -cur.t0 : 0;
       const int hi = a.n_new - cur.t0 < QT ? a.n_new - cur.t0 : QT;
       const uint32_t vm = hi - lo >= 32 ? 0xFFFFFFFFu : (((1u << (hi - lo)) - 1u) << lo);
@@ -517,15 +523,15 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
       if (!in_range) {
         flags |= TQ_FLAG_OUT_OF_RANGE;
       } else {
-        const int64_t hs0 = int64_t(cur.h) * a.t.cap + cur.base;
-        if (t < QT && ((vm >> t) & 1)) *reinterpret_cast<uint32_t *>(a.t.scl + (hs0 + t) * 2) = sm.scl[t];
-        if (a.t.layout == TQ_LAYOUT_BLOCK32) {
+        const int64_t hs0 = int64_t(cur.h) * tt.cap + cur.base;
+        if (t < QT && ((vm >> t) & 1)) *reinterpret_cast<uint32_t *>(tt.scl + (hs0 + t) * 2) = sm.scl[t];
+        if (tt.layout == TQ_LAYOUT_BLOCK32) {
           // the (plane, coordinate) words are the value layout's words of this block
-          const int64_t b0 = int64_t(cur.h) * (a.t.cap / 32) + (cur.base >> 5);
+          const int64_t b0 = int64_t(cur.h) * (tt.cap / 32) + (cur.base >> 5);
           for (int c = t; c < npl * QD; c += QN) {
             const int pl = c / QD, cc = c % QD;
             const uint32_t word = *reinterpret_cast<const uint32_t *>(&sm.wst[pl][cc][0]);
-            uint32_t *dw = pl < BQ ? a.t.idx + (b0 * BQ + pl) * QD + cc : a.t.sgn + b0 * QD + cc;
+            uint32_t *dw = pl < BQ ? tt.idx + (b0 * BQ + pl) * QD + cc : tt.sgn + b0 * QD + cc;
             if (vm == 0xFFFFFFFFu) {
               *dw = word;
             } else {
@@ -542,7 +548,7 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
             uint32_t word = act ? *reinterpret_cast<const uint32_t *>(&sm.wst[pl][32 * wd + row][0]) : 0u;
             word = transpose32(word, row);  // lane row now holds slot base + row
             if (act && ((vm >> row) & 1)) {
-              uint32_t *dw = pl < BQ ? a.t.idx + ((hs0 + row) * BQ + pl) * 4 + wd : a.t.sgn + (hs0 + row) * 4 + wd;
+              uint32_t *dw = pl < BQ ? tt.idx + ((hs0 + row) * BQ + pl) * 4 + wd : tt.sgn + (hs0 + row) * 4 + wd;
               *dw = word;
             }
           }
@@ -560,7 +566,8 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
 template <int BQ, bool F32>
 int launch_q(const QuantArgs &a, hipStream_t s) {
   const int64_t tpb = (int64_t(a.n_new) + QT - 1) / QT + 1;
-  const int64_t n_tiles = int64_t(a.batch) * a.H * tpb;
+  const int64_t n1 = int64_t(a.batch) * a.H * tpb;  // tiles per tensor
+  const int64_t n_tiles = n1 * (a.n_tensor == 2 ? 2 : 1);
   if (n_tiles >= (int64_t(1) << 31)) return 1;
   // Persistent grid of two work-groups per CU, the occupancy the kernel's
   // registers and LDS are sized for; a grid larger than what fits only queues
@@ -575,7 +582,7 @@ int launch_q(const QuantArgs &a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(n_tiles < full ? n_tiles : full);
   if (grid == 0) return 0;
   hipLaunchKernelGGL((quantize_mfma<BQ, F32>), dim3(grid), dim3(QN), 0, s, a, static_cast<uint32_t>(n_tiles),
-                     make_fastdiv(static_cast<uint32_t>(tpb)), make_fastdiv(static_cast<uint32_t>(a.H)));
+                     static_cast<uint32_t>(n1), make_fastdiv(static_cast<uint32_t>(tpb)), make_fastdiv(static_cast<uint32_t>(a.H)));
   return hipGetLastError() != hipSuccess;
 }
 
@@ -666,7 +673,7 @@ __device__ inline void load_rows_w(const QuantArgs &a, const Tile &T, int v, int
   if (tok >= 0 && tok < a.n_new) {
     const size_t row = (size_t(T.b) * a.H + T.h) * size_t(a.n_new) + tok;
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.t.x) + row * WD) + q4;
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(T.tensor ? a.t2.x : a.t.x) + row * WD) + q4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const u32x4 v = __builtin_nontemporal_load(p + 4 * i);
@@ -692,7 +699,7 @@ __device__ inline void load_slice(__amdgpu_buffer_rsrc_t m, int voff, int kc, bf
 }
 
 template <int BQ, int NPI>
-__global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_tiles, FastDiv ftpb, FastDiv fh) {
+__global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_tiles, uint32_t n1, FastDiv ftpb, FastDiv fh) {
   constexpr int L = 1 << BQ;
   constexpr int K = L / 2 - 1;  // positive boundaries
   __shared__ WSmem<BQ> sm;
@@ -719,15 +726,16 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
   uint32_t tile = blockIdx.x;
   Tile T{};
   if (tile < n_tiles) {
-    T = tile_at<WT>(a, tile, ftpb, fh);
+    T = tile_at<WT>(a, tile, n1, ftpb, fh);
     load_rows_w(a, T, v, q4, xr);
   }
   for (; tile < n_tiles; tile += gridDim.x) {
     const Tile cur = T;
+    const QuantTensorArgs &tt = cur.tensor ? a.t2 : a.t;  // this tile's tensor
     const uint32_t nxt = tile + gridDim.x;
     if (cur.t0 >= a.n_new) {  // no token falls in this tile (uniform)
       if (nxt < n_tiles) {
-        T = tile_at<WT>(a, nxt, ftpb, fh);
+        T = tile_at<WT>(a, nxt, n1, ftpb, fh);
         load_rows_w(a, T, v, q4, xr);
       }
       continue;
@@ -786,7 +794,7 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
         if (tok >= 0 && tok < a.n_new) {
           if (nonfinite) flags |= TQ_FLAG_NONFINITE_INPUT;
           if (over) flags |= TQ_FLAG_SCALE_OVERFLOW;
-          if (a.t.dbg) a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2] = nu;
+          if (tt.dbg) tt.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2] = nu;
         }
       }
     }
@@ -900,7 +908,7 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
       for (int kc = 0; kc < WPD; ++kc) load_slice<2>(pst, moff, kc, ps[kc]);
     }
     if (!sk && nxt < n_tiles) {
-      T = tile_at<WT>(a, nxt, ftpb, fh);
+      T = tile_at<WT>(a, nxt, n1, ftpb, fh);
       load_rows_w(a, T, v, q4, xr);
     }
     __syncthreads();
@@ -946,7 +954,7 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
         // the next tile's input: issued after the last matrix slice, since a
         // wait for a slice issued later would also wait for these HBM loads
         if (nxt < n_tiles) {
-          T = tile_at<WT>(a, nxt, ftpb, fh);
+          T = tile_at<WT>(a, nxt, n1, ftpb, fh);
           load_rows_w(a, T, v, q4, xr);
         }
         PlaneBits4 pbs;
@@ -967,13 +975,13 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
           const int tok = cur.t0 + t;
           if (tok >= 0 && tok < a.n_new) {
             if (over) flags |= TQ_FLAG_SCALE_OVERFLOW;
-            if (a.t.dbg) a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = rho;
+            if (tt.dbg) tt.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = rho;
           }
         }
       } else if (t < WT) {
         const int tok = cur.t0 + t;
-        if (tok >= 0 && tok < a.n_new && a.t.dbg)
-          a.t.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = 0.0f;
+        if (tok >= 0 && tok < a.n_new && tt.dbg)
+          tt.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = 0.0f;
       }
       if (t < WT) sm.scl[t] = sm.nub[t] | (rbits << 16);
     }
@@ -991,22 +999,22 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
         const int hi = a.n_new - tb < 32 ? a.n_new - tb : 32;
         vm[blk] = hi <= lo ? 0u : hi - lo >= 32 ? 0xFFFFFFFFu : (((1u << (hi - lo)) - 1u) << lo);
         const int64_t sb = cur.base + 32 * blk;  // base and cap are multiples of 32
-        inr[blk] = sb >= 0 && sb < a.t.cap;
+        inr[blk] = sb >= 0 && sb < tt.cap;
         if (vm[blk] != 0u && !inr[blk]) flags |= TQ_FLAG_OUT_OF_RANGE;
       }
       const int npl = BQ + (sk ? 1 : 0);
-      const int64_t hs0 = int64_t(cur.h) * a.t.cap + cur.base;
+      const int64_t hs0 = int64_t(cur.h) * tt.cap + cur.base;
       if (t < WT && ((vm[t >> 5] >> (t & 31)) & 1) && inr[t >> 5])
-        *reinterpret_cast<uint32_t *>(a.t.scl + (hs0 + t) * 2) = sm.scl[t];
-      if (a.t.layout == TQ_LAYOUT_BLOCK32) {
+        *reinterpret_cast<uint32_t *>(tt.scl + (hs0 + t) * 2) = sm.scl[t];
+      if (tt.layout == TQ_LAYOUT_BLOCK32) {
         // the (plane, block, coordinate) words are the value layout's words
-        const int64_t b0 = int64_t(cur.h) * (a.t.cap / 32) + (cur.base >> 5);
+        const int64_t b0 = int64_t(cur.h) * (tt.cap / 32) + (cur.base >> 5);
         for (int c = t; c < npl * 4 * WD; c += WN) {
           const int pl = c / (4 * WD), blk = (c / WD) & 3, cc = c % WD;
           const uint32_t m = vm[blk];
           if (m == 0u || !inr[blk]) continue;
           const uint32_t word = *reinterpret_cast<const uint32_t *>(&sm.wst[pl][blk][cc][0]);
-          uint32_t *dw = pl < BQ ? a.t.idx + ((b0 + blk) * BQ + pl) * WD + cc : a.t.sgn + (b0 + blk) * WD + cc;
+          uint32_t *dw = pl < BQ ? tt.idx + ((b0 + blk) * BQ + pl) * WD + cc : tt.sgn + (b0 + blk) * WD + cc;
           if (m == 0xFFFFFFFFu) {
             *dw = word;
           } else {
@@ -1023,7 +1031,7 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
           word = transpose32(word, row);  // lane row now holds slot base + 32 blk + row
           if (((vm[blk] >> row) & 1) && inr[blk]) {
             const int64_t slot = hs0 + 32 * blk + row;
-            uint32_t *dw = pl < BQ ? a.t.idx + (slot * BQ + pl) * (WD / 32) + wd : a.t.sgn + slot * (WD / 32) + wd;
+            uint32_t *dw = pl < BQ ? tt.idx + (slot * BQ + pl) * (WD / 32) + wd : tt.sgn + slot * (WD / 32) + wd;
             *dw = word;
           }
         }
@@ -1040,7 +1048,8 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
 template <int BQ>
 int launch_w(const QuantArgs &a, hipStream_t s) {
   const int64_t tpb = (int64_t(a.n_new) + 31 + WT - 1) / WT;
-  const int64_t n_tiles = int64_t(a.batch) * a.H * tpb;
+  const int64_t n1 = int64_t(a.batch) * a.H * tpb;  // tiles per tensor
+  const int64_t n_tiles = n1 * (a.n_tensor == 2 ? 2 : 1);
   if (n_tiles >= (int64_t(1) << 31)) return 1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -1050,7 +1059,7 @@ int launch_w(const QuantArgs &a, hipStream_t s) {
   if (grid == 0) return 0;
   constexpr int NPI = BQ == 3 ? 3 : 2;
   hipLaunchKernelGGL((quantize_wide<BQ, NPI>), dim3(grid), dim3(WN), 0, s, a, static_cast<uint32_t>(n_tiles),
-                     make_fastdiv(static_cast<uint32_t>(tpb)), make_fastdiv(static_cast<uint32_t>(a.H)));
+                     static_cast<uint32_t>(n1), make_fastdiv(static_cast<uint32_t>(tpb)), make_fastdiv(static_cast<uint32_t>(a.H)));
   return hipGetLastError() != hipSuccess;
 }
 
