@@ -180,54 +180,69 @@ __device__ inline void clip_seq(const DecodeArgs &a, int b, int64_t *start, int6
 // in practice the roundings are independent and far smaller); the fp32
 // accumulation adds a few roundings of the partial sums.
 
-// Writes one lane's operand for (plane pidx or the sign plane, word wsl of the
-// slice, product i, slot s) of query head hl of group grp: item enumerates
-// them.  vals holds the slice's 64 coordinates (c0 .. c0 + 63).
-template <int D>
-__device__ void write_query_operand(const DecodeArgs &a, const float *vals, int c0, bool sgn, int npk, int grp_idx,
-                                    int hl, int item) {
-  constexpr int NW = D / 128;
-  const int G = a.G, S = 16 / G, NM = (kQDigits + S - 1) / S;
+// Pass 1, thread (plane p, word wsl of the slice, entry e) of one head: its
+// target T (entry e of lane group "word" is coordinate 32 w + 4 (e & 7) + (e >> 3),
+// whose key bit reads f = 1 for e >> 3 < 2, else 2), the block exponent from the
+// word's largest |T| (the 32 threads of a word are one half of a wave), the
+// fixed-point value F = rint(T 2^E), |F| < 2^24, and its six e2m3 digit codes
+// (sign << 5 | nibble l) as bytes 0..5 of code[p][wsl][e]; E into Ex[p][wsl].
+__device__ inline void query_fixed_point(const DecodeArgs &a, const float *vals, bool sgn, int idx,
+                                         uint2 (*code)[2][32], int (*Ex)[2], int lane) {
+  const int pidx = idx >> 6, wsl = (idx >> 5) & 1, e = idx & 31;
+  const double wk = sgn ? (a.k.sketch ? a.qbase * double(a.kappa) : 0.0) : a.qbase * a.walsh_k[pidx];
+  const float c = static_cast<float>((e >> 3) < 2 ? 2.0 * wk : wk);
+  const float t = c * vals[32 * wsl + 4 * (e & 7) + (e >> 3)];
+  float tmax = fabsf(t);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, lane_xor_f(tmax, o, lane));
+  const int E = tmax > 0.0f ? 23 - ilogbf(tmax) : 0;  // |T| 2^E < 2^24
+  const float Fv = rintf(ldexpf(t, E));                // an integer, exact in fp32
+  uint32_t mag = static_cast<uint32_t>(fabsf(Fv));
+  mag = mag > 0xFFFFFFu ? 0xFFFFFFu : mag;             // rint may reach 2^24
+  const uint32_t sg = Fv < 0.0f ? 0x20202020u : 0u;
+  // nibbles 0..3 and 4..5 of mag, one per byte
+  const uint32_t lo = (mag & 0xFu) | ((mag & 0xF0u) << 4) | ((mag & 0xF00u) << 8) | ((mag & 0xF000u) << 12);
+  const uint32_t hi = ((mag >> 16) & 0xFu) | ((mag >> 12) & 0xF00u);
+  code[pidx][wsl][e] = uint2{lo | sg, hi | (sg & 0x2020u)};
+  if (e == 0) Ex[pidx][wsl] = E;
+}
+
+// Pass 2: one lane's operand for (plane pidx or the sign plane, word wsl of the
+// slice, product i, slot s) of query head hl of group grp_idx (item enumerates
+// them): digit l = S i + s of the 32 entries in 6-bit fields, and its block
+// scale byte.
+template <int D, int G>
+__device__ void pack_query_operand(const DecodeArgs &a, const uint2 (*code)[2][32], const int (*Ex)[2], int c0,
+                                   bool sgn, int npk, int grp_idx, int hl, int item) {
+  constexpr int NW = D / 128, S = 16 / G, NM = (kQDigits + S - 1) / S;
   const int s = item % S, i = (item / S) % NM, wsl = (item / (S * NM)) & 1, pidx = item / (S * NM * 2);
   const int w = c0 / 32 + wsl, g = w & 3, c = w >> 2;
   const int m = 4 * (hl & 3) + S * (hl >> 2) + s, lane = 16 * g + m, l = S * i + s;
-  const double wk = sgn ? (a.k.sketch ? a.qbase * double(a.kappa) : 0.0) : a.qbase * a.walsh_k[pidx];
-  // targets T = (2 w / f) v in fp32: f = 1 for e >> 3 < 2, else 2
-  const float w1 = static_cast<float>(2.0 * wk), w2 = static_cast<float>(wk);
-  const float *v = vals + 32 * wsl;
-  float t[32];
-  float tmax = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    t[e] = ((e >> 3) < 2 ? w1 : w2) * v[4 * (e & 7) + (e >> 3)];
-    tmax = fmaxf(tmax, fabsf(t[e]));
-  }
-  const int E = tmax > 0.0f ? 23 - ilogbf(tmax) : 0;  // |T| 2^E < 2^24
   uint32_t dw[6] = {0u, 0u, 0u, 0u, 0u, 0u};
   if (l < kQDigits) {
+    const uint32_t *cw = reinterpret_cast<const uint32_t *>(code[pidx][wsl]) + (l >> 2);
+    const uint32_t bs = 8 * (l & 3);
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      const float F = rintf(ldexpf(t[e], E));  // an integer below 2^24 in magnitude (exact in fp32)
-      uint32_t mag = static_cast<uint32_t>(fabsf(F));
-      mag = mag > 0xFFFFFFu ? 0xFFFFFFu : mag;  // rint may reach 2^24
-      const uint32_t code = (F < 0.0f ? 32u : 0u) | ((mag >> (4 * l)) & 15u);
+      const uint32_t cd = (cw[2 * e] >> bs) & 63u;
       const int pos = 6 * e, k = pos >> 5, sh = pos & 31;
-      dw[k] |= code << sh;
-      if (sh > 26) dw[k + 1] |= code >> (32 - sh);
+      dw[k] |= cd << sh;
+      if (sh > 26) dw[k + 1] |= cd >> (32 - sh);
     }
   }
   const int slot = sgn ? kSigPlane : pidx;
   uint32_t *op = a.qop + ((((size_t(grp_idx) * 5 + slot) * NW + c) * NM + i) * kWave + lane) * 8;
   *reinterpret_cast<uint4 *>(op) = uint4{dw[0], dw[1], dw[2], dw[3]};
   *reinterpret_cast<uint2 *>(op + 4) = uint2{dw[4], dw[5]};
-  int sc = 127 + 4 * l + 3 - E;
+  int sc = 127 + 4 * l + 3 - Ex[pidx][wsl];
   sc = sc < 0 ? 0 : sc > 254 ? 254 : sc;
   const int pslot = sgn ? npk : pidx;
   a.qscale[(size_t(grp_idx) * kWave + lane) * 32 + (pslot * NW + c) * NM + i] = static_cast<uint8_t>(sc);
 }
 
+template <int G>
 __device__ inline int q_items(const DecodeArgs &a, bool sgn) {
-  const int S = 16 / a.G;
+  constexpr int S = 16 / G;
   return (sgn ? 1 : n_walsh(a.k.bq)) * 2 * ((kQDigits + S - 1) / S) * S;
 }
 
@@ -237,16 +252,18 @@ __device__ inline int q_items(const DecodeArgs &a, bool sgn) {
 // computes its 64 products in fp32 (about 2^-24 relative error, far inside what
 // the scores need) from the transposed matrices, so that a wave's loads are
 // contiguous, and writes this head's rows of its operand entries.
-template <int D>
+template <int D, int G>
 __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   constexpr int NSL = 2 * D / 64, KPT = D / 4;
   __shared__ float q[D];
   __shared__ float part[4][64];
   __shared__ float vals[64];
+  __shared__ uint2 fx[4][2][32];
+  __shared__ int ex[4][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.x / NSL, t = blockIdx.x % NSL;
   const int b = bh / a.Hq, hq = bh % a.Hq;
-  const int kvh = hq / a.G, hl = hq % a.G;
+  const int kvh = hq / G, hl = hq % G;
   const bool sgn = t >= D / 64;
   const int c0 = (sgn ? t - D / 64 : t) * 64;
   // column c0 + lane of Pi^T or S^T, rows wave KPT .. wave KPT + KPT - 1
@@ -263,19 +280,23 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   __syncthreads();
   if (tid < 64) vals[tid] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
   __syncthreads();
-  const int npk = n_walsh(a.k.bq);
-  if (tid < q_items(a, sgn)) write_query_operand<D>(a, vals, c0, sgn, npk, b * a.Hkv + kvh, hl, tid);
+  const int npk = n_walsh(a.k.bq), nplane = sgn ? 1 : npk;
+  if (tid < nplane * 64) query_fixed_point(a, vals, sgn, tid, fx, ex, lane);
+  __syncthreads();
+  if (tid < q_items<G>(a, sgn)) pack_query_operand<D, G>(a, fx, ex, c0, sgn, npk, b * a.Hkv + kvh, hl, tid);
 }
 
 // Query prep for many query heads: block (group of 8 heads, slice t), the same
 // work as decode_qprep_fast for each head, with the slice of the transposed
 // matrix read once for the group.
-template <int D>
+template <int D, int G>
 __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq) {
   constexpr int NSL = 2 * D / 64, KPT = D / 4, HG = 8;
   __shared__ float q[HG][D];
   __shared__ float part[HG][4][64];
   __shared__ float vals[HG][64];
+  __shared__ uint2 fx[HG][4][2][32];
+  __shared__ int ex[HG][4][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = blockIdx.x / NSL, t = blockIdx.x % NSL;
   const bool sgn = t >= D / 64;
@@ -302,12 +323,17 @@ __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq
     vals[h][c] = (part[h][0][c] + part[h][1][c]) + (part[h][2][c] + part[h][3][c]);
   }
   __syncthreads();
-  const int npk = n_walsh(a.k.bq), ni = q_items(a, sgn);
+  const int npk = n_walsh(a.k.bq), nplane = sgn ? 1 : npk, ni = q_items<G>(a, sgn);
+  for (int e = tid; e < HG * nplane * 64; e += 256) {  // whole waves: the per-word maxima stay in a wave
+    const int h = e / (nplane * 64);
+    query_fixed_point(a, vals[h], sgn, e % (nplane * 64), fx[h], ex[h], lane);
+  }
+  __syncthreads();
   for (int e = tid; e < HG * ni; e += 256) {
     const int h = e / ni, bh = grp * HG + h;
     if (bh >= nq) continue;
     const int b = bh / a.Hq, hq = bh % a.Hq;
-    write_query_operand<D>(a, vals[h], c0, sgn, npk, b * a.Hkv + hq / a.G, hq % a.G, e % ni);
+    pack_query_operand<D, G>(a, fx[h], ex[h], c0, sgn, npk, b * a.Hkv + hq / G, hq % G, e % ni);
   }
 }
 
@@ -1179,6 +1205,25 @@ int launch_partial(const DecodeArgs &a, hipStream_t s) {
   }
 }
 
+// Query prep: per-head blocks, or groups of eight heads when there are many.
+template <int D, int G>
+void launch_qprep_g(const DecodeArgs &a, hipStream_t s) {
+  const unsigned nq = static_cast<unsigned>(a.batch * a.Hq);
+  if (nq >= 512)
+    hipLaunchKernelGGL((decode_qprep_grouped<D, G>), dim3((nq + 7) / 8 * (2 * D / 64)), dim3(256), 0, s, a, int(nq));
+  else hipLaunchKernelGGL((decode_qprep_fast<D, G>), dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
+}
+
+template <int D>
+int launch_qprep(const DecodeArgs &a, hipStream_t s) {
+  switch (a.G) {
+    case 4: launch_qprep_g<D, 4>(a, s); return 0;
+    case 8: launch_qprep_g<D, 8>(a, s); return 0;
+    case 16: launch_qprep_g<D, 16>(a, s); return 0;
+    default: return 1;
+  }
+}
+
 // Ring depth of the split pass (slots per wave) for one and two row blocks of
 // heads when the grid is large, so that several work-groups share a CU.
 constexpr int kSlotsRb1 = 2, kSlotsRb2 = 2;
@@ -1186,9 +1231,7 @@ constexpr int kSlotsRb1 = 2, kSlotsRb2 = 2;
 template <int D>
 int launch_fast_d(int rb, const DecodeArgs &a, hipStream_t s, bool sparse) {
   const unsigned nq = static_cast<unsigned>(a.batch * a.Hq);
-  if (nq >= 512)
-    hipLaunchKernelGGL(decode_qprep_grouped<D>, dim3((nq + 7) / 8 * (2 * D / 64)), dim3(256), 0, s, a, int(nq));
-  else hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
+  if (launch_qprep<D>(a, s)) return 1;
   // one head block and at most about two work-groups per CU: a deep ring (two
   // chunks in flight per wave) and two operand buffers
   const bool deep = int64_t(a.n_split) * a.Hkv * a.batch <= 1024;
@@ -1221,10 +1264,7 @@ int launch_score_bq(const DecodeArgs &a, hipStream_t s) {
 
 template <int D>
 int launch_score_d(const DecodeArgs &a, hipStream_t s) {
-  const unsigned nq = static_cast<unsigned>(a.batch * a.Hq);
-  if (nq >= 512)
-    hipLaunchKernelGGL(decode_qprep_grouped<D>, dim3((nq + 7) / 8 * (2 * D / 64)), dim3(256), 0, s, a, int(nq));
-  else hipLaunchKernelGGL(decode_qprep_fast<D>, dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
+  if (launch_qprep<D>(a, s)) return 1;
   const bool deep = int64_t(a.n_split) * a.Hkv * a.batch <= 1024;
   // groups of 16 queries (four row blocks) at d = 128, where their operands fit
   // in registers: each expansion of a key plane then feeds four MFMAs
