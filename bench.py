@@ -512,7 +512,7 @@ def roofline_decode(w, packed_bytes, d_avg):
 
 def bench_context(args, w, s, rot, proj):
     """Workloads 1, 2, 5: a step quantizes the whole context (K and V of every kv
-    head: one tq_quantize_kv call, two equal launches of the quantize kernel) and
+    head: one tq_quantize_kv call, one launch of the quantize kernel for both) and
     then decodes once over a cache written several steps earlier."""
     import torch
     import workloads as W
@@ -549,7 +549,7 @@ def bench_context(args, w, s, rot, proj):
         kc, vc = caches[r]
         if evs is not None:
             evs[0].record(stream)
-        s.quantize(Ks[r], Vs[r], dst, kc, vc, stream=stream)   # two launches: K, then V
+        s.quantize(Ks[r], Vs[r], dst, kc, vc, stream=stream)   # one launch: K and V tiles
         if evs is not None:
             evs[1].record(stream)
         kd, vd = caches[(r + R // 2) % R]
@@ -563,9 +563,8 @@ def bench_context(args, w, s, rot, proj):
     assert torch.isfinite(out).all(), "decode produced non-finite output"
 
     q_avg, d_avg = float(qt.mean()), float(dt_.mean())
-    # one launch of the quantize kernel: the call runs two equal launches (K, V)
-    # back to back, so a launch takes half the call (its short gap included)
-    ql_avg = q_avg / 2
+    # one launch of the quantize kernel: K and V share one launch (the same spec)
+    ql_avg = q_avg
     q_bytes = in_bytes + packed_bytes
     q_flops = 2 * B * H * T * 4 * d * d           # two d x d contractions per vector
     roof_dec = roofline_decode(w, packed_bytes, d_avg)
@@ -575,13 +574,13 @@ def bench_context(args, w, s, rot, proj):
     note = (f"algorithmic 4 d^2 flops per vector; executed as {pieces} bf16 piece products per vector "
             f"({pieces - 3} for Pi x, 3 for the sketch)")
     qkern = "quantize_mfma" if d == 128 else "quantize_wide"
-    ql_bytes, ql_flops = q_bytes / 2, q_flops / 2
+    ql_bytes, ql_flops = q_bytes, q_flops
     ql_gbs, ql_tf = ql_bytes / ql_avg / 1e9, ql_flops / ql_avg / 1e12
     q_traffic = traffic_for([("quantize", 1)], w.name)
     hbm_view = {"achieved": ql_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ql_gbs / HBM_PEAK_GBS}
     mfma_view = {"achieved": ql_tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": ql_tf / BF16_MFMA_PEAK_TFLOPS, "flops_per_launch": ql_flops, "note": note}
-    kdesc = f"{qkern}: one launch per tensor (K or V), {B * H * T} vectors"
+    kdesc = f"{qkern}: one launch for K and V, {2 * B * H * T} vectors"
     if ql_flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > ql_bytes / (HBM_PEAK_GBS * 1e9):
         roof_q = {"bound": "mfma", **{k: v for k, v in mfma_view.items() if k != "note"}, "traffic": q_traffic,
                   "kernel": kdesc, "bytes_per_launch": ql_bytes, "avg_launch_s": ql_avg, "note": note,
@@ -710,8 +709,8 @@ def bench_decode_step(args, w, s, rot, proj):
         "quantize_tokens_per_s": B / q_avg, "quantize_GBps": q_bytes / q_avg / 1e9,
         "decode_call_s": d_avg, "quantize_call_s": q_avg,
         "roofline": roof_dec, "roofline_decode": roof_dec,
-        "roofline_quantize": {"bound": "launch", "kernel": "quantize_mfma: one launch per tensor, "
-                              f"{B * H} vectors", "bytes_per_call": q_bytes, "avg_call_s": q_avg,
+        "roofline_quantize": {"bound": "launch", "kernel": "quantize_mfma: one launch for K and V, "
+                              f"{2 * B * H} vectors", "bytes_per_call": q_bytes, "avg_call_s": q_avg,
                               "note": "a few dozen vectors per call: bound by launch latency, not by a roofline"},
     }
 
@@ -802,8 +801,9 @@ def main():
         "config": r.pop("config"),
         "decode_pct_hbm_peak": 100 * dec_gbs / HBM_PEAK_GBS,
         "hbm_copy_GBps": copy_gbs, "decode_frac_of_copy": dec_gbs / copy_gbs,
-        "compute": "quantize: bf16-piece MFMA, fp32 accumulate; decode: exact int8 MFMA, int32 "
-                   "accumulate, fp32/fp64 softmax and merge",
+        "compute": "quantize: bf16-piece MFMA, fp32 accumulate; decode: scores on fp6 (query digits) x fp4 "
+                   "(key bits) scaled MFMA, fp32 accumulate; values on exact int8 MFMA, int32 accumulate; "
+                   "fp32/fp64 softmax and merge",
         **r, "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:
