@@ -61,7 +61,7 @@ struct DecodePlan {
   int32_t fast;          // 1: matrix-core kernels; 0: reference-grade kernels
   int32_t rb;            // row blocks of 16 (= G / 4) in the matrix-core kernels
   size_t off_qr, off_qs, off_part, off_qop, off_qscale, off_smax, total;  // workspace byte offsets
-  int32_t part_stride;   // floats per partial record: 2 + d + m
+  int32_t part_stride;   // floats per partial record: 4 + d + m (matrix-core layout; the reference kernels use 2 + d + m)
 };
 
 DecodePlan decode_plan(const tq_config &cfg, int32_t batch, int32_t max_len);

@@ -51,6 +51,11 @@ typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kSigPlane = 4;     // operand / accumulator slot of the sign plane
 
+// Floats per split partial record: m, l, two pad words, A [D], B [D] ((A, B) start
+// 16-byte aligned, for 16-byte loads in the merge).
+template <int D>
+constexpr int part_stride() { return 4 + 2 * D; }
+
 __device__ inline int n_walsh(int bq) { return bq == 3 ? 4 : bq; }
 
 __device__ inline float load_q(const void *x, int dtype, size_t i) {
@@ -286,12 +291,14 @@ __global__ __launch_bounds__(256) void decode_qprep_fast(DecodeArgs a) {
   if (tid < q_items<G>(a, sgn)) pack_query_operand<D, G>(a, fx, ex, c0, sgn, npk, b * a.Hkv + kvh, hl, tid);
 }
 
-// Query prep for many query heads: block (group of 8 heads, slice t), the same
+constexpr int kQPrepGroup = 4;  // query heads per block of the grouped query prep
+
+// Query prep for many query heads: block (group of kQPrepGroup heads, slice t), the same
 // work as decode_qprep_fast for each head, with the slice of the transposed
 // matrix read once for the group.
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_qprep_grouped(DecodeArgs a, int nq) {
-  constexpr int NSL = 2 * D / 64, KPT = D / 4, HG = 8;
+  constexpr int NSL = 2 * D / 64, KPT = D / 4, HG = kQPrepGroup;
   __shared__ float q[HG][D];
   __shared__ float part[HG][4][64];
   __shared__ float vals[HG][64];
@@ -479,7 +486,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
   const int64_t lo = abase > start ? abase : start;
   const int64_t hi = (abase + S) < (start + len) ? (abase + S) : (start + len);
   const int bh0 = b * a.Hq + h * G;
-  const int stride = 2 + 2 * D;
+  constexpr int stride = part_stride<D>();
   if (lo >= hi) {
     if (MODE == kAttend && tid < G) {
       float *o = a.part + (size_t(bh0 + tid) * a.n_split + split) * stride;
@@ -921,8 +928,8 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
       double acc = 0.0;
 #pragma unroll
       for (int p = 0; p < PV; ++p) acc += a.walsh_v[p] * pm_form(av[p][nb][rb], ak[0][rb]);
-      o[2 + j0 + nb] = static_cast<float>(ldexp(acc, -Ew));
-      o[2 + D + j0 + nb] = skv ? static_cast<float>(ldexp(pm_form(av[PV][nb][rb], ak[1][rb]), -Ewp)) : 0.0f;
+      o[4 + j0 + nb] = static_cast<float>(ldexp(acc, -Ew));
+      o[4 + D + j0 + nb] = skv ? static_cast<float>(ldexp(pm_form(av[PV][nb][rb], ak[1][rb]), -Ewp)) : 0.0f;
     }
     if (wave == 0 && col == 0) {
       o[0] = mh[rb] * 0.69314718055994531f;  // natural-log units for the merge
@@ -933,66 +940,70 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
 
 // ----------------------------------------------------------------- merge ---
 // out = (Pi^T A + kappa S^T B) / l, where (A, B) and l merge the split partials
-// by log-sum-exp.  Block (head, cs) computes the CPB x 64 outputs from 64 CPB cs
-// on (CPB = d / 64, one block per head, when there are heads enough to fill the
-// chip; else CPB = 1):
+// by log-sum-exp.  A partial record is m, l, two pad words, A [d], B [d]
+// (kPartStride floats, so that (A, B) start 16-byte aligned).  Block (head, cs)
+// computes the CPB x 64 outputs from 64 CPB cs on (CPB = d / 64, one block per
+// head, when there are heads enough to fill the chip; else CPB = 1):
 //  1. the split maxima and sums: M = max m_s over splits with tokens, weights
 //     w_s = exp(m_s - M) (0 for a split with no tokens, whose (A, B) are
 //     unwritten), l = sum w_s l_s; the weights go to LDS.
-//  2. thread (sg, e) sums w_s x_s for element e of (A, B) over splits sg,
-//     sg + SGN, ...; its loads are issued before step 1 (they do not depend on
-//     the weights), as are the matrix loads of step 3.  The split groups are
-//     added in LDS.
-//  3. per group of 64 columns, thread (kq, jj) takes rows kq, kq + 8, ... of
-//     [Pi ; S] (2 d rows) at the group's column jj; the 8 row groups are added
-//     in LDS.
+//  2. thread (sg, c) sums w_s x_s for the 16-byte chunk c of (A, B) over splits
+//     sg, sg + SGN, ...; its loads are issued before step 1 (they do not depend
+//     on the weights), as are the matrix loads of step 3.  The split groups are
+//     added in LDS, kappa B formed there.
+//  3. per group of 64 columns, thread (kq, jj) takes entries kq 2d/8 ..
+//     (kq + 1) 2d/8 - 1 of [A ; kappa B] against the matching row segment of
+//     Pi^T (rows of A) or S^T (rows of B), both read as 16-byte chunks of the
+//     transposed matrices; the 8 partial sums are added in LDS.
 // Every block of a head recomputes steps 1-2 so that no block waits on another.
 constexpr int kMaxSplits = 2048;
 
 template <int D, int CPB>
 __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
-  // split groups; split loads per chunk (all of a long context's splits at once where
-  // there are heads enough to fill the chip, fewer registers otherwise)
-  constexpr int NT = 512, SGN = NT / (2 * D), CHS = D == 128 && CPB > 1 ? 64 : 32;
-  constexpr int RPT = 2 * D / 8;                         // matrix rows per thread
-  // matrix columns loaded at the start: every group's when they fit in registers
-  constexpr int PRE = CPB * RPT <= 64 ? CPB : 1;
+  constexpr int NT = 512, NC4 = 2 * D / 4, SGN = NT / NC4;  // chunks of (A, B), split groups
+  constexpr int CHS = D == 128 ? 16 : 20;                      // split loads per thread and round
+  constexpr int KR = 2 * D / 8, KR4 = KR / 4;                 // step 3: entries per thread
+  constexpr int stride = part_stride<D>();
   __shared__ float ws_l[kMaxSplits], ls_l[kMaxSplits];
   __shared__ float red[8];
-  __shared__ float accg[SGN][2 * D];
+  __shared__ __attribute__((aligned(16))) float4 accg[SGN][NC4];
+  __shared__ __attribute__((aligned(16))) float vec[2 * D];
   __shared__ float prj[8][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int ncs = D / (64 * CPB);
   const int bh = blockIdx.x / ncs, cs = blockIdx.x % ncs;
-  const int stride = 2 + 2 * D, ns = a.n_split;
+  const int ns = a.n_split;
   const float *base = a.part + size_t(bh) * ns * stride;
-  // step 3's matrix column: rows kq + 8 i of [Pi ; S]
+  // step 3's matrix rows: column col of the output = row col of Pi^T / S^T,
+  // entries kq KR .. kq KR + KR - 1 of [A ; B] (kq < 4: Pi^T; else S^T)
   const int jj = tid & 63, kq = tid >> 6;
-  float mrow[PRE][RPT];
-  auto load_rows = [&](int g, int col) {
+  const float *mt = kq < 4 ? a.rotT : a.projT;
+  const int k0 = (kq & 3) * KR;
+  float4 mrow[KR4];
+  auto load_rows = [&](int col) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int k = kq + 8 * i;
-      mrow[g][i] = k < D ? a.rot[size_t(k) * D + col] : a.proj[size_t(k - D) * D + col];
+    for (int i = 0; i < KR4; ++i) mrow[i] = *reinterpret_cast<const float4 *>(mt + size_t(col) * D + k0 + 4 * i);
+  };
+  load_rows(64 * CPB * cs + jj);
+  // step 2's first round of loads
+  const int c4 = tid % NC4, sg = tid / NC4;
+  float4 x[CHS];
+  auto load_x = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < CHS; ++u) {
+      const int sp = s0 + sg + SGN * u;
+      x[u] = sp < ns ? *reinterpret_cast<const float4 *>(base + size_t(sp) * stride + 4 + 4 * c4)
+                     : float4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
-#pragma unroll
-  for (int g = 0; g < PRE; ++g) load_rows(g, 64 * (CPB * cs + g) + jj);
-  // step 2's first chunk of elements
-  const int e = tid % (2 * D), sg = tid / (2 * D);
-  float x[CHS];
-#pragma unroll
-  for (int u = 0; u < CHS; ++u) {
-    const int s = sg + SGN * u;
-    x[u] = s < ns ? base[size_t(s) * stride + 2 + e] : 0.0f;
-  }
+  load_x(0);
   // step 1
   float mmax = -INFINITY;
-  for (int s = tid; s < ns; s += NT) {
-    const float ms = base[size_t(s) * stride], ls = base[size_t(s) * stride + 1];
-    ws_l[s] = ls > 0.0f ? ms : -INFINITY;
-    ls_l[s] = ls > 0.0f ? ls : 0.0f;
-    mmax = fmaxf(mmax, ws_l[s]);
+  for (int sp = tid; sp < ns; sp += NT) {
+    const float2 ml = *reinterpret_cast<const float2 *>(base + size_t(sp) * stride);
+    ws_l[sp] = ml.y > 0.0f ? ml.x : -INFINITY;
+    ls_l[sp] = ml.y > 0.0f ? ml.y : 0.0f;
+    mmax = fmaxf(mmax, ws_l[sp]);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, lane_xor_f(mmax, o, lane));
@@ -1003,11 +1014,11 @@ __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
   for (int w = 1; w < 8; ++w) M = fmaxf(M, red[w]);
   __syncthreads();
   float lsum = 0.0f;
-  for (int s = tid; s < ns; s += NT) {
-    const float ms = ws_l[s];
+  for (int sp = tid; sp < ns; sp += NT) {
+    const float ms = ws_l[sp];
     const float w = ms > -INFINITY ? expf(ms - M) : 0.0f;
-    lsum = fmaf(w, ls_l[s], lsum);
-    ws_l[s] = w;
+    lsum = fmaf(w, ls_l[sp], lsum);
+    ws_l[sp] = w;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) lsum += lane_xor_f(lsum, o, lane);
@@ -1017,59 +1028,56 @@ __global__ __launch_bounds__(512) void decode_merge_fast(DecodeArgs a) {
 #pragma unroll
   for (int w = 0; w < 8; ++w) l += red[w];
   // step 2
-  float acc = 0.0f;
+  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = 0; s0 < ns; s0 += SGN * CHS) {
-    if (s0 > 0)
-#pragma unroll
-      for (int u = 0; u < CHS; ++u) {
-        const int s = s0 + sg + SGN * u;
-        x[u] = s < ns ? base[size_t(s) * stride + 2 + e] : 0.0f;
-      }
+    if (s0 > 0) load_x(s0);
 #pragma unroll
     for (int u = 0; u < CHS; ++u) {
-      const int s = s0 + sg + SGN * u;
-      const float w = s < ns ? ws_l[s] : 0.0f;
-      acc = w > 0.0f ? fmaf(w, x[u], acc) : acc;  // a split without tokens has stale (A, B)
+      const int sp = s0 + sg + SGN * u;
+      const float w = sp < ns ? ws_l[sp] : 0.0f;
+      if (w > 0.0f) {  // a split without tokens has stale (A, B)
+        acc.x = fmaf(w, x[u].x, acc.x);
+        acc.y = fmaf(w, x[u].y, acc.y);
+        acc.z = fmaf(w, x[u].z, acc.z);
+        acc.w = fmaf(w, x[u].w, acc.w);
+      }
     }
   }
-  accg[sg][e] = e < D ? acc : a.kappa * acc;
+  accg[sg][c4] = acc;
+  __syncthreads();
+  if (tid < 2 * D) {
+    const float *ag = reinterpret_cast<const float *>(accg);
+    float v = 0.0f;
+#pragma unroll
+    for (int g = 0; g < SGN; ++g) v += ag[g * 2 * D + tid];
+    vec[tid] = tid < D ? v : a.kappa * v;
+  }
   __syncthreads();
   // step 3
-  float v[RPT];
+  float4 vk[KR4];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    v[i] = 0.0f;
-#pragma unroll
-    for (int g = 0; g < SGN; ++g) v[i] += accg[g][kq + 8 * i];
-  }
-  auto project = [&](int cg, const float (&mr)[RPT]) {
-    const int col0 = 64 * (CPB * cs + cg);
+  for (int i = 0; i < KR4; ++i) vk[i] = *reinterpret_cast<const float4 *>(&vec[kq * KR + 4 * i]);
+#pragma unroll 1
+  for (int cg = 0; cg < CPB; ++cg) {
+    if (cg > 0) {
+      load_rows(64 * (CPB * cs + cg) + jj);
+      __syncthreads();  // prj of the previous group has been read
+    }
     float pj = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) pj = fmaf(mr[i], v[i], pj);
+    for (int i = 0; i < KR4; ++i) {
+      pj = fmaf(mrow[i].x, vk[i].x, pj);
+      pj = fmaf(mrow[i].y, vk[i].y, pj);
+      pj = fmaf(mrow[i].z, vk[i].z, pj);
+      pj = fmaf(mrow[i].w, vk[i].w, pj);
+    }
     prj[kq][jj] = pj;
     __syncthreads();
     if (tid < 64) {
       float o = 0.0f;
 #pragma unroll
       for (int g = 0; g < 8; ++g) o += prj[g][tid];
-      a.out[size_t(bh) * D + col0 + tid] = l > 0.0f ? o / l : 0.0f;
-    }
-  };
-  if constexpr (PRE > 1) {
-#pragma unroll
-    for (int cg = 0; cg < CPB; ++cg) {
-      if (cg > 0) __syncthreads();  // prj of the previous group has been read
-      project(cg, mrow[cg]);
-    }
-  } else {
-#pragma unroll 1
-    for (int cg = 0; cg < CPB; ++cg) {
-      if (cg > 0) {
-        load_rows(0, 64 * (CPB * cs + cg) + jj);
-        __syncthreads();  // prj of the previous group has been read
-      }
-      project(cg, mrow[0]);
+      a.out[size_t(bh) * D + 64 * (CPB * cs + cg) + tid] = l > 0.0f ? o / l : 0.0f;
     }
   }
 }
@@ -1088,7 +1096,8 @@ __global__ __launch_bounds__(512) void decode_merge_grouped(DecodeArgs a, int nq
   __shared__ float prj[HG][8][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = blockIdx.x;
-  const int stride = 2 + 2 * D, ns = a.n_split;
+  constexpr int stride = part_stride<D>();
+  const int ns = a.n_split;
   // the projection's first matrix column group, rows kq + 8 i of [Pi ; S], issued first
   const int jj = lane, kq = wave;
   float mrow[RPT];
@@ -1120,12 +1129,14 @@ __global__ __launch_bounds__(512) void decode_merge_grouped(DecodeArgs a, int nq
           const float *p = base + size_t(s) * stride;
           pm[u] = p[0];
           pl[u] = p[1];
-          // element 2 + e sits 8 bytes past a 16-byte boundary: float2 pairs
+          // (A, B) start 16 bytes into the record: 16-byte chunks
 #pragma unroll
-          for (int e = 0; e < EPT; e += 2) {
-            const float2 v2 = *reinterpret_cast<const float2 *>(p + 2 + lane * EPT + e);
-            x[u][e] = v2.x;
-            x[u][e + 1] = v2.y;
+          for (int e = 0; e < EPT; e += 4) {
+            const float4 v4 = *reinterpret_cast<const float4 *>(p + 4 + lane * EPT + e);
+            x[u][e] = v4.x;
+            x[u][e + 1] = v4.y;
+            x[u][e + 2] = v4.z;
+            x[u][e + 3] = v4.w;
           }
         }
       }
@@ -1205,12 +1216,13 @@ int launch_partial(const DecodeArgs &a, hipStream_t s) {
   }
 }
 
-// Query prep: per-head blocks, or groups of eight heads when there are many.
+// Query prep: per-head blocks, or groups of kQPrepGroup heads when there are many.
 template <int D, int G>
 void launch_qprep_g(const DecodeArgs &a, hipStream_t s) {
   const unsigned nq = static_cast<unsigned>(a.batch * a.Hq);
   if (nq >= 512)
-    hipLaunchKernelGGL((decode_qprep_grouped<D, G>), dim3((nq + 7) / 8 * (2 * D / 64)), dim3(256), 0, s, a, int(nq));
+    hipLaunchKernelGGL((decode_qprep_grouped<D, G>), dim3((nq + kQPrepGroup - 1) / kQPrepGroup * (2 * D / 64)),
+                       dim3(256), 0, s, a, int(nq));
   else hipLaunchKernelGGL((decode_qprep_fast<D, G>), dim3(nq * (2 * D / 64)), dim3(256), 0, s, a);
 }
 
