@@ -64,11 +64,14 @@ struct QSmem {
   __align__(16) uint16_t wst[BQ + 1][QD][2]; // words (plane, coordinate), bit = row; plane BQ: signs
   __align__(16) uint32_t nub[QT];            // fp16 bits of ||x||
   __align__(16) uint32_t scl[QT];            // nu bits | rho bits << 16
+  int64_t gslot[QT];                          // gather tiles: destination slot per row (-1: none)
+  int32_t ghead[QT];                          // gather tiles: head per row
 };
 
 struct Tile {
   int b, h;
   int tensor;     // 0: QuantArgs::t, 1: QuantArgs::t2
+  uint32_t g0;    // gather tiles: first vector of the flattened [batch][H][n_new] list
   int t0;         // token of row 0 (negative when the tile starts before the first token)
   int64_t base;   // slot of row 0, a multiple of 32
 };
@@ -114,13 +117,58 @@ __device__ inline Tile tile_at(const QuantArgs &a, uint32_t tile, uint32_t n1, F
   return T;
 }
 
+// Gather tiles, for appends of a few tokens per sequence: tile k of a tensor holds
+// vectors 32 k .. 32 k + 31 of the flattened [batch][H][n_new] list, whatever
+// their sequences and heads, so that no matrix work goes to empty rows.
+__device__ inline Tile gather_tile_at(uint32_t tile, uint32_t n1) {
+  Tile T{};
+  T.tensor = tile >= n1 ? 1 : 0;
+  T.g0 = (T.tensor ? tile - n1 : tile) * QT;
+  return T;
+}
+
+// Row v of a tile: whether it holds a vector, that vector's index in the input
+// ([batch][H][n_new] flattened), its head and its destination slot.  fn divides
+// by n_new (gather tiles only).
+struct Row {
+  bool valid;
+  size_t i;
+  int h;
+  int64_t slot;
+};
+
+template <bool GATHER>
+__device__ inline Row row_at(const QuantArgs &a, const Tile &T, int v, FastDiv fn, FastDiv fh) {
+  Row r;
+  if (GATHER) {
+    // the flattened list holds fewer than 2^31 vectors (checked at launch)
+    const uint32_t n = uint32_t(a.batch) * uint32_t(a.H) * uint32_t(a.n_new);
+    const uint32_t i = T.g0 + v;
+    r.valid = i < n;
+    const uint32_t ic = r.valid ? i : 0u;  // every read stays inside dst
+    const uint32_t bh = fdiv(ic, fn);
+    const uint32_t b = fdiv(bh, fh);
+    r.i = ic;
+    r.h = static_cast<int>(bh - b * fh.d);
+    r.slot = a.dst[b] + int64_t(ic - bh * fn.d);
+  } else {
+    const int tok = T.t0 + v;
+    r.valid = tok >= 0 && tok < a.n_new;
+    r.i = (size_t(T.b) * a.H + T.h) * size_t(a.n_new) + tok;
+    r.h = T.h;
+    r.slot = T.base + v;
+  }
+  return r;
+}
+
 // Row v, coordinates 16 c16 .. 16 c16 + 15 of a tile (zeros outside the tokens).
-template <bool F32>
-__device__ inline void load_rows(const QuantArgs &a, const Tile &T, int v, int c16, uint4 *r) {
+template <bool F32, bool GATHER>
+__device__ inline void load_rows(const QuantArgs &a, const Tile &T, int v, int c16, uint4 *r, FastDiv fn,
+                                 FastDiv fh) {
   constexpr int NV = F32 ? 4 : 2;
-  const int tok = T.t0 + v;
-  if (tok >= 0 && tok < a.n_new) {
-    const size_t row = (size_t(T.b) * a.H + T.h) * size_t(a.n_new) + tok;
+  const Row rw = row_at<GATHER>(a, T, v, fn, fh);
+  if (rw.valid) {
+    const size_t row = rw.i;
     const void *x = T.tensor ? a.t2.x : a.t.x;
     const uint4 *p = F32 ? reinterpret_cast<const uint4 *>(static_cast<const float *>(x) + row * QD + 16 * c16)
                          : reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + row * QD + 16 * c16);
@@ -211,7 +259,8 @@ struct PlaneBits {
   }
 };
 
-template <int BQ, bool F32>
+// GATHER: tiles of the flattened vector list (ftpb then divides by n_new).
+template <int BQ, bool F32, bool GATHER>
 __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_tiles, uint32_t n1, FastDiv ftpb, FastDiv fh) {
   constexpr int NPX = F32 ? 3 : 1;
   constexpr int NV = F32 ? 4 : 2;
@@ -266,9 +315,10 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
   uint4 xr[NV];
   uint32_t tile = blockIdx.x;
   Tile T{};
+  auto tile_of = [&](uint32_t k) { return GATHER ? gather_tile_at(k, n1) : tile_at<QT>(a, k, n1, ftpb, fh); };
   if (tile < n_tiles) {
-    T = tile_at<QT>(a, tile, n1, ftpb, fh);
-    load_rows<F32>(a, T, v, c16, xr);
+    T = tile_of(tile);
+    load_rows<F32, GATHER>(a, T, v, c16, xr, ftpb, fh);
   }
   for (; tile < n_tiles; tile += gridDim.x) {
     const Tile cur = T;
@@ -278,10 +328,11 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
     for (int i = 0; i < NV; ++i) xc[i] = xr[i];
     const uint32_t nxt = tile + gridDim.x;
     if (nxt < n_tiles) {
-      T = tile_at<QT>(a, nxt, n1, ftpb, fh);
-      load_rows<F32>(a, T, v, c16, xr);
+      T = tile_of(nxt);
+      load_rows<F32, GATHER>(a, T, v, c16, xr, ftpb, fh);
     }
-    if (cur.t0 >= a.n_new) continue;  // no token falls in this tile (uniform)
+    // no token falls in this tile (uniform)
+    if (GATHER ? cur.g0 >= uint32_t(a.batch) * uint32_t(a.H) * uint32_t(a.n_new) : cur.t0 >= a.n_new) continue;
 
     // ---------------------------------------------------------------- A --
     {
@@ -349,11 +400,11 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
       sm.vth[v][c16] = c16 < 4 ? (c16 < K && nu > 0.0f ? nu * vcoef : INFINITY) : n16 * vcoef;
       if (c16 == 0) {
         sm.nub[v] = nb;
-        const int tok = cur.t0 + v;
-        if (tok >= 0 && tok < a.n_new) {
+        const Row rw = row_at<GATHER>(a, cur, v, ftpb, fh);
+        if (rw.valid) {
           if (nonfinite) flags |= TQ_FLAG_NONFINITE_INPUT;
           if (over) flags |= TQ_FLAG_SCALE_OVERFLOW;
-          if (tt.dbg) tt.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2] = nu;
+          if (tt.dbg) tt.dbg[size_t(rw.i) * 2] = nu;
         }
       }
     }
@@ -498,23 +549,67 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
           const float rho = __builtin_amdgcn_sqrtf(rr);
           bool over = false;
           rbits = f16_bits_f32(rho, &over);
-          const int tok = cur.t0 + t;
-          if (tok >= 0 && tok < a.n_new) {
+          const Row rw = row_at<GATHER>(a, cur, t, ftpb, fh);
+          if (rw.valid) {
             if (over) flags |= TQ_FLAG_SCALE_OVERFLOW;
-            if (tt.dbg) tt.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = rho;
+            if (tt.dbg) tt.dbg[size_t(rw.i) * 2 + 1] = rho;
           }
         }
       } else if (t < QT) {
-        const int tok = cur.t0 + t;
-        if (tok >= 0 && tok < a.n_new && tt.dbg)
-          tt.dbg[((int64_t(cur.b) * a.H + cur.h) * a.n_new + tok) * 2 + 1] = 0.0f;
+        const Row rw = row_at<GATHER>(a, cur, t, ftpb, fh);
+        if (rw.valid && tt.dbg) tt.dbg[size_t(rw.i) * 2 + 1] = 0.0f;
       }
       if (t < QT) sm.scl[t] = sm.nub[t] | (rbits << 16);
+      if (GATHER && t < QT) {
+        // each row's destination for phase E (read there after the barrier below;
+        // rewritten only in the next tile's phase D)
+        const Row rw = row_at<GATHER>(a, cur, t, ftpb, fh);
+        const bool ok = rw.valid && rw.slot >= 0 && rw.slot < tt.cap;
+        if (rw.valid && !ok) flags |= TQ_FLAG_OUT_OF_RANGE;
+        sm.gslot[t] = ok ? rw.slot : -1;
+        sm.ghead[t] = rw.h;
+      }
     }
     __syncthreads();
 
     // ---------------------------------------------------------------- E --
-    {
+    if constexpr (GATHER) {
+      // rows go to their own slots: scales and token-major records per row; in the
+      // value layout one bit per (row, plane, coordinate) word, set or cleared by
+      // one atomic (other rows of the same 32-slot block may be written at once)
+      const int npl = BQ + (sk ? 1 : 0);
+      if (t < QT && sm.gslot[t] >= 0)
+        *reinterpret_cast<uint32_t *>(tt.scl + (int64_t(sm.ghead[t]) * tt.cap + sm.gslot[t]) * 2) = sm.scl[t];
+      if (tt.layout == TQ_LAYOUT_BLOCK32) {
+        for (int c = t; c < npl * QD; c += QN) {
+          const int pl = c / QD, cc = c % QD;
+          const uint32_t word = *reinterpret_cast<const uint32_t *>(&sm.wst[pl][cc][0]);
+          for (int r = 0; r < QT; ++r) {
+            const int64_t sl = sm.gslot[r];
+            if (sl < 0) continue;
+            const int64_t b0 = int64_t(sm.ghead[r]) * (tt.cap / 32) + (sl >> 5);
+            uint32_t *dw = pl < BQ ? tt.idx + (b0 * BQ + pl) * QD + cc : tt.sgn + b0 * QD + cc;
+            const uint32_t bit = 1u << (sl & 31);
+            if ((word >> r) & 1u) atomicOr(dw, bit);
+            else atomicAnd(dw, ~bit);
+          }
+        }
+      } else {
+        for (int b2 = 0; b2 < npl * 4; b2 += 2 * QW) {
+          const int blk = b2 + 2 * w + (lane >> 5), row = lane & 31;
+          const int pl = blk >> 2, wd = blk & 3;
+          const bool act = blk < npl * 4;
+          uint32_t word = act ? *reinterpret_cast<const uint32_t *>(&sm.wst[pl][32 * wd + row][0]) : 0u;
+          word = transpose32(word, row);  // lane row now holds row `row`'s word
+          const int64_t sl = sm.gslot[row];
+          if (act && sl >= 0) {
+            const int64_t hs = int64_t(sm.ghead[row]) * tt.cap + sl;
+            uint32_t *dw = pl < BQ ? tt.idx + (hs * BQ + pl) * 4 + wd : tt.sgn + hs * 4 + wd;
+            *dw = word;
+          }
+        }
+      }
+    } else {
       const bool in_range = cur.base >= 0 && cur.base < tt.cap;  // base and cap are multiples of 32
       const int lo = cur.t0 < 0 ? -cur.t0 : 0;
       const int hi = a.n_new - cur.t0 < QT ? a.n_new - cur.t0 : QT;
@@ -563,10 +658,23 @@ __global__ __launch_bounds__(QN, 2) void quantize_mfma(QuantArgs a, uint32_t n_t
   }
 }
 
+// Appends of at most kGatherMaxNew tokens per sequence run on gather tiles when
+// they fill at least kGatherMinTiles tiles per tensor.  Fewer vectors go faster on
+// one tile per (sequence, head), spread over as many work-groups: a gather tile's
+// value records cost 32 x 384 bit updates (atomics) in one work-group, and the
+// per-CU atomic rate then sets its time (one-off A/B on the box, one token per
+// sequence and 8 heads, K and V: 4 sequences 9.9 us per-sequence tiles against
+// 20.8 us gather; 64 sequences 25.7 against 21.4; 512 sequences 138 against 22).
+constexpr int kGatherMaxNew = 4;
+constexpr int kGatherMinTiles = 8;
+
 template <int BQ, bool F32>
 int launch_q(const QuantArgs &a, hipStream_t s) {
+  const int64_t nvec = int64_t(a.batch) * a.H * a.n_new;  // vectors per tensor
+  const bool gather = a.n_new <= kGatherMaxNew && nvec >= int64_t(kGatherMinTiles) * QT && nvec < (int64_t(1) << 31);
   const int64_t tpb = (int64_t(a.n_new) + QT - 1) / QT + 1;
-  const int64_t n1 = int64_t(a.batch) * a.H * tpb;  // tiles per tensor
+  const int64_t n1 = gather ? (int64_t(a.batch) * a.H * a.n_new + QT - 1) / QT  // tiles per tensor
+                            : int64_t(a.batch) * a.H * tpb;
   const int64_t n_tiles = n1 * (a.n_tensor == 2 ? 2 : 1);
   if (n_tiles >= (int64_t(1) << 31)) return 1;
   // Persistent grid of two work-groups per CU, the occupancy the kernel's
@@ -581,8 +689,14 @@ int launch_q(const QuantArgs &a, hipStream_t s) {
   const int64_t full = int64_t(per_cu) * cus;
   const unsigned grid = static_cast<unsigned>(n_tiles < full ? n_tiles : full);
   if (grid == 0) return 0;
-  hipLaunchKernelGGL((quantize_mfma<BQ, F32>), dim3(grid), dim3(QN), 0, s, a, static_cast<uint32_t>(n_tiles),
-                     static_cast<uint32_t>(n1), make_fastdiv(static_cast<uint32_t>(tpb)), make_fastdiv(static_cast<uint32_t>(a.H)));
+  if (gather)
+    hipLaunchKernelGGL((quantize_mfma<BQ, F32, true>), dim3(grid), dim3(QN), 0, s, a, static_cast<uint32_t>(n_tiles),
+                       static_cast<uint32_t>(n1), make_fastdiv(static_cast<uint32_t>(a.n_new)),
+                       make_fastdiv(static_cast<uint32_t>(a.H)));
+  else
+    hipLaunchKernelGGL((quantize_mfma<BQ, F32, false>), dim3(grid), dim3(QN), 0, s, a, static_cast<uint32_t>(n_tiles),
+                       static_cast<uint32_t>(n1), make_fastdiv(static_cast<uint32_t>(tpb)),
+                       make_fastdiv(static_cast<uint32_t>(a.H)));
   return hipGetLastError() != hipSuccess;
 }
 

@@ -642,6 +642,35 @@ def test_adjacent_sequences_share_blocks(wid):
     assert run.status() == 0
 
 
+@pytest.mark.parametrize("wid", [2, 3])
+def test_gather_appends(wid):
+    """Appends of one to four tokens to 40 sequences at once run on gather tiles
+    (rows of different sequences and heads in one tile; value bits set or cleared by
+    one atomic each) and leave the same cache bytes as one call per sequence.  The
+    sequences' ranges are adjacent and unpadded, so rows of one call share 32-slot
+    value blocks (checked without the oracle; the per-sequence calls are parity-tested
+    against it)."""
+    w = W.WORKLOADS[wid]
+    B, n = 40, 70
+    run = Run(w, batch=B, n_tokens=n)
+    dst = np.arange(B, dtype=np.int64) * n + 5
+    assert int(dst[-1]) + n <= run.cap
+    for b in range(B):
+        run.quantize(K=run.K[b:b + 1], V=run.V[b:b + 1], dst=dst[b:b + 1])
+    apart = [x.copy() for c in run.host_caches() for x in c if x is not None]
+    for c in (run.kc, run.vc):
+        c.idx.zero_(); c.sgn.zero_(); c.scl.zero_()
+    off = 0
+    for m in (1, 2, 3, 4) * 7:
+        run.quantize(K=run.K[:, :, off:off + m], V=run.V[:, :, off:off + m], dst=dst + off)
+        off += m
+    assert off == n
+    together = [x for c in run.host_caches() for x in c if x is not None]
+    for a, b in zip(apart, together):
+        np.testing.assert_array_equal(a, b)
+    assert run.status() == 0
+
+
 @pytest.mark.parametrize("wid,batch,T", [(2, 2, 3000), (3, 2, 2500), (5, 2, 1500), (4, 3, 5000)])
 def test_sparse_v(wid, batch, T):
     """Sparse V decode against the oracle's attention_sparse_v over the same packed
