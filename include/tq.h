@@ -70,7 +70,9 @@ typedef enum {
   TQ_ERR_NO_CONVERGENCE = -5 /* Lloyd-Max did not converge                   */
 } tq_status;
 
-typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+/* TQ_DTYPE_RANGE_ widens the enum's range to all of int32, so that reading any
+ * value a caller passes (and rejecting it with TQ_ERR_INVALID_ARG) is defined. */
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_DTYPE_RANGE_ = -2147483647 - 1 } tq_dtype;
 
 /* Cache layouts (bit k of a uint32 word is its k-th least significant bit;
  * index plane q holds bit q of the cell index; a sign bit is 1 for (S r)_i >= 0):
