@@ -563,8 +563,10 @@ def bench_context(args, w, s, rot, proj):
     assert torch.isfinite(out).all(), "decode produced non-finite output"
 
     q_avg, d_avg = float(qt.mean()), float(dt_.mean())
-    # one launch of the quantize kernel: K and V share one launch (the same spec)
-    ql_avg = q_avg
+    # one launch of the quantize kernel: at d = 128 K and V share one launch (the
+    # same spec); at d = 256 the call makes one launch per tensor
+    nql = 1 if d == 128 else 2
+    ql_avg = q_avg / nql
     q_bytes = in_bytes + packed_bytes
     q_flops = 2 * B * H * T * 4 * d * d           # two d x d contractions per vector
     roof_dec = roofline_decode(w, packed_bytes, d_avg)
@@ -574,13 +576,14 @@ def bench_context(args, w, s, rot, proj):
     note = (f"algorithmic 4 d^2 flops per vector; executed as {pieces} bf16 piece products per vector "
             f"({pieces - 3} for Pi x, 3 for the sketch)")
     qkern = "quantize_mfma" if d == 128 else "quantize_wide"
-    ql_bytes, ql_flops = q_bytes, q_flops
+    ql_bytes, ql_flops = q_bytes / nql, q_flops // nql
     ql_gbs, ql_tf = ql_bytes / ql_avg / 1e9, ql_flops / ql_avg / 1e12
     q_traffic = traffic_for([("quantize", 1)], w.name)
     hbm_view = {"achieved": ql_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ql_gbs / HBM_PEAK_GBS}
     mfma_view = {"achieved": ql_tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": ql_tf / BF16_MFMA_PEAK_TFLOPS, "flops_per_launch": ql_flops, "note": note}
-    kdesc = f"{qkern}: one launch for K and V, {2 * B * H * T} vectors"
+    kdesc = (f"{qkern}: one launch for K and V, {2 * B * H * T} vectors" if nql == 1 else
+             f"{qkern}: one launch per tensor (two per call), {B * H * T} vectors")
     if ql_flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > ql_bytes / (HBM_PEAK_GBS * 1e9):
         roof_q = {"bound": "mfma", **{k: v for k, v in mfma_view.items() if k != "note"}, "traffic": q_traffic,
                   "kernel": kdesc, "bytes_per_launch": ql_bytes, "avg_launch_s": ql_avg, "note": note,

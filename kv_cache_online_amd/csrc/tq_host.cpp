@@ -429,9 +429,11 @@ int tq_quantize_kv(const tq_config *cfg, const void *k, const void *v, tq_dtype 
   a.n_tensor = 1;
   if (k && v) {
     // K and V with one spec (bits, sketch, codebook) share one launch of the
-    // matrix-core kernel: its set-up (the matrices into registers) is paid once
+    // d = 128 matrix-core kernel: its set-up (the matrices into registers) is paid
+    // once.  (The d = 256 kernel streams its matrices and has no registers to spare
+    // for a second tensor's arguments: one launch per tensor there.)
     const tq::QuantTensorArgs tk = tensor_args(0), tv = tensor_args(1);
-    if (fast_ok(tk) && tk.bq == tv.bq && tk.sketch == tv.sketch &&
+    if (cfg->d == 128 && fast_ok(tk) && tk.bq == tv.bq && tk.sketch == tv.sketch &&
         std::memcmp(&tk.cb, &tv.cb, sizeof(tk.cb)) == 0) {
       a.t = tk;
       a.t2 = tv;

@@ -787,7 +787,7 @@ __device__ inline void load_rows_w(const QuantArgs &a, const Tile &T, int v, int
   if (tok >= 0 && tok < a.n_new) {
     const size_t row = (size_t(T.b) * a.H + T.h) * size_t(a.n_new) + tok;
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(T.tensor ? a.t2.x : a.t.x) + row * WD) + q4;
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.t.x) + row * WD) + q4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const u32x4 v = __builtin_nontemporal_load(p + 4 * i);
@@ -845,7 +845,7 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
   }
   for (; tile < n_tiles; tile += gridDim.x) {
     const Tile cur = T;
-    const QuantTensorArgs &tt = cur.tensor ? a.t2 : a.t;  // this tile's tensor
+    const QuantTensorArgs &tt = a.t;  // one tensor per launch at d = 256
     const uint32_t nxt = tile + gridDim.x;
     if (cur.t0 >= a.n_new) {  // no token falls in this tile (uniform)
       if (nxt < n_tiles) {
@@ -1161,9 +1161,10 @@ __global__ __launch_bounds__(WN, 1) void quantize_wide(QuantArgs a, uint32_t n_t
 
 template <int BQ>
 int launch_w(const QuantArgs &a, hipStream_t s) {
+  if (a.n_tensor != 1) return 1;  // one tensor per launch at d = 256 (its registers are full)
   const int64_t tpb = (int64_t(a.n_new) + 31 + WT - 1) / WT;
-  const int64_t n1 = int64_t(a.batch) * a.H * tpb;  // tiles per tensor
-  const int64_t n_tiles = n1 * (a.n_tensor == 2 ? 2 : 1);
+  const int64_t n1 = int64_t(a.batch) * a.H * tpb;
+  const int64_t n_tiles = n1;
   if (n_tiles >= (int64_t(1) << 31)) return 1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
