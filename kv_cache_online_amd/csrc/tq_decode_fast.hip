@@ -395,12 +395,20 @@ __device__ inline unsigned lds_addr(const void *p) {
 // accesses it cannot tell apart from the ring.  The instructions have no
 // register results; the LDS they write is read only after an explicit vmcnt
 // wait (wait_vm), and no load is issued into a slot before this wave's reads
-// of it are complete (lgkmcnt(0) first).
+// of it are complete (lgkmcnt(0) first).  NT: a non-temporal load, for data
+// that the launch reads once (attention streams each cache line once, and the
+// stream then displaces less of what is still to be read, such as the split
+// partials the merge reads next).  Key scoring reads the same keys from every
+// query group's blocks and keeps ordinary loads.
+template <bool NT>
 __device__ inline void dma16(u4 r, unsigned dst, int voff, int soff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(dst) : "memory");
+  if (NT) asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(dst) : "memory");
+  else asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(dst) : "memory");
 }
+template <bool NT>
 __device__ inline void dma4(u4 r, unsigned dst, int voff, int soff) {
-  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(dst) : "memory");
+  if (NT) asm volatile("buffer_load_dword %0, %1, %2 offen nt lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(dst) : "memory");
+  else asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(dst) : "memory");
 }
 
 // Wait until at most N vector-memory loads of this wave are outstanding.  The
@@ -455,7 +463,7 @@ constexpr int kAttend = 0, kScores = 1, kMaxima = 2;
 
 template <int D, int RB, int BQK, int BQV, int SLOTS, int AWP_, int MODE = kAttend, bool SPARSE = false>
 __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
-  constexpr bool SCORES = MODE == kScores, KEYS_ONLY = MODE != kAttend;
+  constexpr bool SCORES = MODE == kScores, KEYS_ONLY = MODE != kAttend, NT = !SCORES;
   using P = SplitShape<D, RB, BQK, BQV, SLOTS, AWP_>;
   constexpr int W = P::W, NB = P::NB, NW = P::NW, G = P::G, PK = P::PK, PV = P::PV;
   constexpr int KREC = P::KREC, KSREC = P::KSREC, VREC = P::VREC, VSREC = P::VSREC, AWP = P::AWP;
@@ -526,11 +534,11 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
     if (s < nk) {
       const int tile = wave + 4 * s;
 #pragma unroll
-      for (int i = 0; i < BQK * NW; ++i) dma16(rk, dst + 1024 * i, tile * 64 * KREC + 1024 * i + 16 * lane, 0);
+      for (int i = 0; i < BQK * NW; ++i) dma16<NT>(rk, dst + 1024 * i, tile * 64 * KREC + 1024 * i + 16 * lane, 0);
 #pragma unroll
-      for (int i = 0; i < NW; ++i) dma16(rks, dst + P::K_SG + 1024 * i, tile * 64 * KSREC + 1024 * i + 16 * lane, 0);
-      dma4(rkc, dst + P::K_KS, tile * 256 + 4 * lane, 0);
-      dma4(rvc, dst + P::K_VS, tile * 256 + 4 * lane, 0);
+      for (int i = 0; i < NW; ++i) dma16<NT>(rks, dst + P::K_SG + 1024 * i, tile * 64 * KSREC + 1024 * i + 16 * lane, 0);
+      dma4<NT>(rkc, dst + P::K_KS, tile * 256 + 4 * lane, 0);
+      dma4<NT>(rvc, dst + P::K_VS, tile * 256 + 4 * lane, 0);
     } else {
       const int r = s - nk;
 #pragma unroll
@@ -540,7 +548,7 @@ __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
           const bool sg = p == BQV;
           const int rec = sg ? VSREC : VREC;
           const int voff = (8 * r + 4 * i + vblkl) * rec + (sg ? 0 : p * D * 4) + wave * D + 16 * vpiece;
-          dma16(sg ? rvs : rv, dst + p * P::VPL + 1024 * i, voff, 0);
+          dma16<NT>(sg ? rvs : rv, dst + p * P::VPL + 1024 * i, voff, 0);
         }
     }
   };
