@@ -399,7 +399,8 @@ __device__ inline unsigned lds_addr(const void *p) {
 // that the launch reads once (attention streams each cache line once, and the
 // stream then displaces less of what is still to be read, such as the split
 // partials the merge reads next).  Key scoring reads the same keys from every
-// query group's blocks and keeps ordinary loads.
+// query group's blocks, and the Sparse V maxima pass reads keys that attention
+// reads again: both keep ordinary loads.
 template <bool NT>
 __device__ inline void dma16(u4 r, unsigned dst, int voff, int soff) {
   if (NT) asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(dst) : "memory");
@@ -463,7 +464,9 @@ constexpr int kAttend = 0, kScores = 1, kMaxima = 2;
 
 template <int D, int RB, int BQK, int BQV, int SLOTS, int AWP_, int MODE = kAttend, bool SPARSE = false>
 __global__ __launch_bounds__(256) void decode_partial_fast(DecodeArgs a) {
-  constexpr bool SCORES = MODE == kScores, KEYS_ONLY = MODE != kAttend, NT = !SCORES;
+  // non-temporal loads where this pass is the last to read the stream: attention
+  // (not the Sparse V maxima pass, whose keys the attention pass reads again)
+  constexpr bool SCORES = MODE == kScores, KEYS_ONLY = MODE != kAttend, NT = MODE == kAttend;
   using P = SplitShape<D, RB, BQK, BQV, SLOTS, AWP_>;
   constexpr int W = P::W, NB = P::NB, NW = P::NW, G = P::G, PK = P::PK, PV = P::PV;
   constexpr int KREC = P::KREC, KSREC = P::KSREC, VREC = P::VREC, VSREC = P::VSREC, AWP = P::AWP;
